@@ -1,0 +1,38 @@
+"""fp64 CPU oracle of the block-sparse 3D attention path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package imports, calls or
+links this package; only the tests, the smoke check and the bench's CPU
+baseline leg use it.  It shares no code with the HIP path: it is plain NumPy
+written from the pages' definitions, slow and obviously correct.
+
+Sources cited in the modules:
+  [SVG]      Sparse VideoGen article (m.jxzklqfsx.com/article/815093)
+  [CalibAtt] calibrated sparse attention article (lpnh.cn/news/568491)
+  [VDA]      video-diffusion acceleration survey (wmrh.cn/news/48564)
+  [SparsePR] SparsePR tutorial (lqnn.cn/news/72918)
+
+Every function here is pinned by a CPU test to facts other than itself; none is
+"parity unpinned".
+"""
+from .layout import token_major_index, to_token_major, to_frame_major
+from .masks import (
+    block_of_layout, spatial_block_mask, temporal_block_mask, apply_text_rule,
+    online_candidate_masks, anchor_rows, anchor_query_blocks, restrict_to_anchor_blocks,
+)
+from .attention import dense_attention, block_masked_attention, head_attention
+from .encode import encode_masks, decode_masks, iv_capacity
+from .profiler import profile_heads, profile_errors_decomposed
+from .calibrate import calibrate_row, calibrate_mask
+from .broadcast import row_broadcast
+from .flops import kept_pairs, algorithmic_flops
+
+__all__ = [
+    "token_major_index", "to_token_major", "to_frame_major",
+    "block_of_layout", "spatial_block_mask", "temporal_block_mask", "apply_text_rule",
+    "online_candidate_masks", "anchor_rows", "anchor_query_blocks", "restrict_to_anchor_blocks",
+    "dense_attention", "block_masked_attention", "head_attention",
+    "encode_masks", "decode_masks", "iv_capacity",
+    "profile_heads", "profile_errors_decomposed",
+    "calibrate_row", "calibrate_mask", "row_broadcast",
+    "kept_pairs", "algorithmic_flops",
+]
