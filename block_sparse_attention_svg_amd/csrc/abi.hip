@@ -1,0 +1,267 @@
+// C ABI of libsvg: host-side argument validation, then kernel launches.
+// Validation happens before any HIP call, so every error path can be checked
+// without a GPU.  The library allocates nothing and keeps no state besides a
+// thread-local error message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "svg_internal.h"
+
+namespace svg {
+
+static thread_local char g_err[512] = "";
+
+svg_status fail(svg_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+svg_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SVG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SVG_OK;
+}
+
+namespace {
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int n_blocks(const svg_shape& s) { return ceil_div(s.N, s.block); }
+
+svg_status check_shape(const svg_shape& s, const char* fn) {
+  if (s.B < 1 || s.H < 1 || s.N < 1 || s.D < 1)
+    return fail(SVG_ERR_INVALID_ARG, "%s: B, H, N, D must be positive (got %d, %d, %d, %d)", fn,
+                s.B, s.H, s.N, s.D);
+  if (s.F < 1 || s.Hs < 1 || s.Ws < 1)
+    return fail(SVG_ERR_INVALID_ARG, "%s: F, Hs, Ws must be positive", fn);
+  if (int64_t(s.F) * s.Hs * s.Ws > s.N)
+    return fail(SVG_ERR_INVALID_ARG, "%s: F*Hs*Ws = %lld exceeds N = %d", fn,
+                (long long)(int64_t(s.F) * s.Hs * s.Ws), s.N);
+  if (s.block != 64 && s.block != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: block must be 64 or 128 (got %d)", fn, s.block);
+  if (int64_t(s.B) * s.H > 65535)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: B*H = %lld exceeds 65535", fn, (long long)(int64_t(s.B) * s.H));
+  if (s.N > (1 << 30)) return fail(SVG_ERR_UNSUPPORTED, "%s: N = %d exceeds 2^30", fn, s.N);
+  return SVG_OK;
+}
+
+svg_status check_head_dim(const svg_shape& s, const char* fn) {
+  if (s.D != 64 && s.D != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128 (got %d)", fn, s.D);
+  return SVG_OK;
+}
+
+svg_status check_mask(const svg_mask* m, const svg_shape& s, const char* fn, int want_masks) {
+  if (!m) return fail(SVG_ERR_INVALID_ARG, "%s: mask struct is NULL", fn);
+  if (!m->bitmap || !m->row_ptr || !m->iv)
+    return fail(SVG_ERR_INVALID_ARG, "%s: mask bitmap / row_ptr / iv is NULL", fn);
+  if (m->n_masks < 1) return fail(SVG_ERR_INVALID_ARG, "%s: n_masks must be >= 1", fn);
+  if (want_masks > 0 && m->n_masks != want_masks)
+    return fail(SVG_ERR_INVALID_ARG, "%s: expected %d masks, got %d", fn, want_masks, m->n_masks);
+  int nB = n_blocks(s);
+  if (m->n_qb != nB || m->n_kb != nB)
+    return fail(SVG_ERR_INVALID_ARG, "%s: mask is %d x %d blocks, shape needs %d x %d", fn,
+                m->n_qb, m->n_kb, nB, nB);
+  return SVG_OK;
+}
+
+bool overlaps(const void* a, const void* b, size_t bytes) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + bytes && y < x + bytes;
+}
+
+}  // namespace
+}  // namespace svg
+
+using namespace svg;
+
+extern "C" {
+
+const char* svg_status_string(svg_status st) {
+  switch (st) {
+    case SVG_OK: return "SVG_OK";
+    case SVG_ERR_INVALID_ARG: return "SVG_ERR_INVALID_ARG";
+    case SVG_ERR_UNSUPPORTED: return "SVG_ERR_UNSUPPORTED";
+    case SVG_ERR_CAPACITY: return "SVG_ERR_CAPACITY";
+    case SVG_ERR_HIP: return "SVG_ERR_HIP";
+  }
+  return "SVG_ERR_UNKNOWN";
+}
+
+const char* svg_last_error(void) { return g_err; }
+
+const char* svg_version(void) { return "svg-mi355x 0.1 gfx950"; }
+
+svg_status svg_build_masks(svg_shape s, int band_w, uint8_t* masks, void* stream) {
+  const char* fn = "svg_build_masks";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (!masks) return fail(SVG_ERR_INVALID_ARG, "%s: masks is NULL", fn);
+  if (band_w < 0) return fail(SVG_ERR_INVALID_ARG, "%s: band_w must be >= 0", fn);
+  launch_build_masks(s, band_w, masks, as_stream(stream));
+  return check_launch(fn);
+}
+
+int64_t svg_encode_iv_capacity(int n_masks, int n_qb, int n_kb) {
+  if (n_masks < 1 || n_qb < 1 || n_kb < 1) return 0;
+  return int64_t(n_masks) * n_qb * ((n_kb + 1) / 2);
+}
+
+svg_status svg_encode_mask(const uint8_t* dense, int n_masks, int n_qb, int n_kb, uint32_t* bitmap,
+                           int32_t* row_ptr, int32_t* iv, int64_t iv_capacity, void* stream) {
+  const char* fn = "svg_encode_mask";
+  if (!dense || !bitmap || !row_ptr || !iv)
+    return fail(SVG_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  if (n_masks < 1 || n_qb < 1 || n_kb < 1)
+    return fail(SVG_ERR_INVALID_ARG, "%s: n_masks, n_qb, n_kb must be positive", fn);
+  if (int64_t(n_masks) * n_qb > (1 << 28))
+    return fail(SVG_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  int64_t need = svg_encode_iv_capacity(n_masks, n_qb, n_kb);
+  if (iv_capacity < need)
+    return fail(SVG_ERR_CAPACITY, "%s: iv_capacity %lld below worst case %lld", fn,
+                (long long)iv_capacity, (long long)need);
+  if (need > (int64_t(1) << 31) - 1)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: interval count exceeds int32", fn);
+  launch_encode(dense, n_masks, n_qb, n_kb, bitmap, row_ptr, iv, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_permute(const void* x, void* y, svg_dtype dt, svg_shape s, const int32_t* head_sel,
+                       int inverse, void* stream) {
+  const char* fn = "svg_permute";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (!x || !y) return fail(SVG_ERR_INVALID_ARG, "%s: x or y is NULL", fn);
+  if (dt != SVG_BF16 && dt != SVG_F32) return fail(SVG_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  int esz = dt == SVG_BF16 ? 2 : 4;
+  if (s.D != 64 && s.D != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128 (got %d)", fn, s.D);
+  size_t bytes = size_t(s.B) * s.H * s.N * s.D * esz;
+  if (overlaps(x, y, bytes)) return fail(SVG_ERR_INVALID_ARG, "%s: x and y overlap", fn);
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: x and y must be 16-byte aligned", fn);
+  launch_permute(x, y, esz, s, head_sel, inverse, as_stream(stream));
+  return check_launch(fn);
+}
+
+size_t svg_profile_workspace_bytes(svg_shape s, int n_samples) {
+  if (check_shape(s, "svg_profile_workspace_bytes") != SVG_OK) return 0;
+  return profile_workspace_bytes(s.B * s.H, s.N, s.D, s.block, n_samples, nullptr, nullptr);
+}
+
+svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_shape s, float scale,
+                             const int32_t* idx, int n_samples, const svg_mask* cand,
+                             int32_t* choice, float* err, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const char* fn = "svg_profile_heads";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (!q || !k || !v || !idx || !choice)
+    return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / v / idx / choice", fn);
+  if (n_samples < 1 || n_samples > 64)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: n_samples must be in [1, 64] (got %d)", fn, n_samples);
+  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
+  if (svg_status st = check_mask(cand, s, fn, 2)) return st;
+  int nB = n_blocks(s);
+  int W = ceil_div(nB, 32);
+  if (W > 32) return fail(SVG_ERR_UNSUPPORTED, "%s: more than 1024 blocks per row", fn);
+  int chunk_keys = 0, n_chunks = 0;
+  size_t need = profile_workspace_bytes(s.B * s.H, s.N, s.D, s.block, n_samples, &chunk_keys, &n_chunks);
+  if (!workspace || workspace_bytes < need)
+    return fail(SVG_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  ProfileArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.idx = idx;
+  a.n_samples = n_samples;
+  a.bitmap = cand->bitmap;
+  a.nB = nB;
+  a.W = W;
+  a.choice = choice;
+  a.err = err;
+  a.ws = static_cast<float*>(workspace);
+  a.BH = s.B * s.H;
+  a.N = s.N; a.D = s.D; a.block = s.block;
+  a.F = s.F; a.Hs = s.Hs; a.Ws = s.Ws;
+  a.chunk_keys = chunk_keys;
+  a.n_chunks = n_chunks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  launch_profile(a, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
+                                 const void* qp, const void* kp, const void* vp, void* op,
+                                 svg_shape s, float scale, const svg_mask* masks,
+                                 const int32_t* head_mask, const int32_t* head_layout, float* lse,
+                                 void* stream) {
+  const char* fn = "svg_block_sparse_attn";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (!q || !k || !v || !o) return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / v / o", fn);
+  if (head_layout && (!qp || !kp || !vp || !op))
+    return fail(SVG_ERR_INVALID_ARG, "%s: head_layout given but a token-major twin is NULL", fn);
+  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
+  if (svg_status st = check_mask(masks, s, fn, 0)) return st;
+  size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
+  if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
+    return fail(SVG_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.qp = qp; a.kp = kp; a.vp = vp; a.op = op;
+  a.row_ptr = masks->row_ptr;
+  a.iv = masks->iv;
+  a.n_masks = masks->n_masks;
+  a.n_qb = masks->n_qb;
+  a.n_kb = masks->n_kb;
+  a.head_mask = head_mask;
+  a.head_layout = head_layout;
+  a.lse = lse;
+  a.BH = s.B * s.H;
+  a.N = s.N; a.D = s.D; a.block = s.block;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  launch_attn(a, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_row_broadcast(void* o, svg_shape s, const int32_t* head_sel, int k_anchors,
+                             void* stream) {
+  const char* fn = "svg_row_broadcast";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (!o) return fail(SVG_ERR_INVALID_ARG, "%s: o is NULL", fn);
+  if (k_anchors < 1 || k_anchors > s.Hs)
+    return fail(SVG_ERR_INVALID_ARG, "%s: k_anchors must be in [1, Hs]", fn);
+  if (reinterpret_cast<uintptr_t>(o) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: o must be 16-byte aligned", fn);
+  launch_row_broadcast(o, s, head_sel, k_anchors, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_restrict_anchor_rows(uint8_t* masks, int n_masks, svg_shape s, const int32_t* mask_sel,
+                                    int k_anchors, void* stream) {
+  const char* fn = "svg_restrict_anchor_rows";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (!masks) return fail(SVG_ERR_INVALID_ARG, "%s: masks is NULL", fn);
+  if (n_masks < 1 || n_masks > 65535) return fail(SVG_ERR_INVALID_ARG, "%s: bad n_masks", fn);
+  if (k_anchors < 1 || k_anchors > s.Hs)
+    return fail(SVG_ERR_INVALID_ARG, "%s: k_anchors must be in [1, Hs]", fn);
+  launch_restrict_anchor_rows(masks, n_masks, s, mask_sel, k_anchors, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_calibrate_masks(const double* energy, int n_masks, int n_qb, int n_kb, double eps,
+                               uint8_t* out, void* stream) {
+  const char* fn = "svg_calibrate_masks";
+  if (!energy || !out) return fail(SVG_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  if (n_masks < 1 || n_qb < 1 || n_kb < 1)
+    return fail(SVG_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+  if (n_kb > 4096) return fail(SVG_ERR_UNSUPPORTED, "%s: n_kb above 4096", fn);
+  if (int64_t(n_masks) * n_qb > 0x7fffffff) return fail(SVG_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (!(eps > 0.0 && eps <= 1.0)) return fail(SVG_ERR_INVALID_ARG, "%s: eps must be in (0, 1]", fn);
+  launch_calibrate(energy, n_masks, n_qb, n_kb, eps, out, as_stream(stream));
+  return check_launch(fn);
+}
+
+}  // extern "C"

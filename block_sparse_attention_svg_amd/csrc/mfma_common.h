@@ -1,0 +1,51 @@
+// Shared device helpers of the attention and profiling kernels: MFMA operand
+// types, 16-byte LDS tiles with an XOR swizzle, and 8x8 bf16 transposes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 b) { return __builtin_bit_cast(uint4, b); }
+
+// A row-major tile of ROWS x COLS bf16 in LDS, stored as 16-byte chunks
+// (8 elements).  Chunk c of row r lives at chunk position c ^ swz(r), where
+// swz spreads the 16 rows read by one MFMA operand fetch over all 64 banks.
+template <int ROWS, int COLS>
+struct LdsTile {
+  static constexpr int CPR = COLS / 8;                    // chunks per row
+  static constexpr int RPC = (16 / CPR) > 0 ? 16 / CPR : 1;  // rows per 256-byte bank sweep
+  static constexpr int CHUNKS = ROWS * CPR;
+  __device__ static __forceinline__ int slot(int r, int c) {
+    return r * CPR + (c ^ ((r / RPC) % CPR));
+  }
+};
+
+// Transpose an 8x8 block of bf16: in[i] holds row i (8 elements, element e in
+// 16-bit half e%2 of word e/2); out[j] receives column j.
+__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t a = (&in[2 * p].x)[j >> 1];
+      uint32_t b = (&in[2 * p + 1].x)[j >> 1];
+      w[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    out[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+}  // namespace svg

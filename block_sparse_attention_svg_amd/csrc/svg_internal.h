@@ -1,0 +1,83 @@
+// Internal declarations shared by the HIP sources of libsvg (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/svg.h"
+
+namespace svg {
+
+// ---- error reporting (abi.hip) -------------------------------------------
+svg_status fail(svg_status st, const char* fmt, ...);
+svg_status check_launch(const char* what);
+
+// ---- small helpers ---------------------------------------------------------
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Division of non-negative int32 values by a run-time constant divisor with a
+// multiply-high and a shift (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", 1994): q = (umulhi(n, magic) + n) >> shift,
+// exact for 0 <= n < 2^31 and 1 <= d < 2^31.
+struct FastDiv {
+  uint32_t d, magic, shift;
+  FastDiv() : d(1), magic(1), shift(0) {}
+  explicit FastDiv(uint32_t divisor) : d(divisor) {
+    shift = 0;
+    while (shift < 32 && (1u << shift) < divisor) ++shift;
+    uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << shift) - divisor)) / divisor + 1;
+    magic = uint32_t(m);
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    uint32_t t = __umulhi(n, magic);
+    return (t + n) >> shift;
+  }
+};
+
+// ---- launchers (one per source file) ----------------------------------------
+void launch_build_masks(const svg_shape& s, int band_w, uint8_t* masks, hipStream_t st);
+void launch_restrict_anchor_rows(uint8_t* masks, int n_masks, const svg_shape& s,
+                                 const int32_t* mask_sel, int k, hipStream_t st);
+void launch_calibrate(const double* E, int n_masks, int n_qb, int n_kb, double eps,
+                      uint8_t* out, hipStream_t st);
+void launch_encode(const uint8_t* dense, int n_masks, int n_qb, int n_kb, uint32_t* bitmap,
+                   int32_t* row_ptr, int32_t* iv, hipStream_t st);
+void launch_permute(const void* x, void* y, int elem_bytes, const svg_shape& s,
+                    const int32_t* head_sel, int inverse, hipStream_t st);
+void launch_row_broadcast(void* o, const svg_shape& s, const int32_t* head_sel, int k,
+                          hipStream_t st);
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  void* o;
+  const void *qp, *kp, *vp;
+  void* op;
+  const int32_t* row_ptr;
+  const int32_t* iv;
+  int n_masks, n_qb, n_kb;
+  const int32_t* head_mask;
+  const int32_t* head_layout;
+  float* lse;
+  int BH, N, D, block;
+  float scale_log2;  // softmax scale times log2(e)
+};
+void launch_attn(const AttnArgs& a, hipStream_t st);
+
+struct ProfileArgs {
+  const void *q, *k, *v;
+  const int32_t* idx;
+  int n_samples;
+  const uint32_t* bitmap;  // [2][nB][W]
+  int nB, W;
+  int32_t* choice;
+  float* err;
+  float* ws;
+  int BH, N, D, block, F, Hs, Ws;
+  int chunk_keys, n_chunks;
+  float scale_log2;
+};
+size_t profile_workspace_bytes(int BH, int N, int D, int block, int n_samples,
+                               int* chunk_keys, int* n_chunks);
+void launch_profile(const ProfileArgs& a, hipStream_t st);
+
+}  // namespace svg

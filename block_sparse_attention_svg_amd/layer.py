@@ -1,0 +1,101 @@
+"""Attention-layer drivers built from the C ABI calls.
+
+OnlineSparseAttention follows the Sparse VideoGen flow ([SVG], online
+profiling and layout transformation): profile the heads on sampled queries,
+move the temporal heads to token-major order, run block-sparse attention with
+each head's chosen mask, move those heads' outputs back.  The head choice
+stays on the device: the same `choice` array selects the permuted heads, the
+mask and the layout, so nothing returns to the host inside a call.
+
+StaticSparseAttention follows the calibrated-mask flow ([CalibAtt] sections
+3.1-3.3): one fixed encoded mask per head, and anchor-row broadcast for the
+row-repetitive heads.
+"""
+import math
+
+import numpy as np
+import torch
+
+from .ops import (Shape, EncodedMasks, svg_build_masks, svg_encode_mask, svg_permute,
+                  svg_profile_workspace_bytes, svg_profile_heads, svg_block_sparse_attn,
+                  svg_row_broadcast, svg_restrict_anchor_rows)
+
+
+class OnlineSparseAttention:
+    def __init__(self, s: Shape, band_w: int, scale: float = None, n_samples: int = 64,
+                 device="cuda"):
+        self.s = s
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(s.D)
+        self.n_samples = n_samples
+        self.dense_masks = svg_build_masks(s, band_w, device=device)
+        self.cand = svg_encode_mask(self.dense_masks)
+        self.workspace = torch.empty(svg_profile_workspace_bytes(s, n_samples), dtype=torch.uint8,
+                                     device=device)
+        self.choice = torch.zeros(s.B * s.H, dtype=torch.int32, device=device)
+        self.err = torch.zeros((s.B * s.H, 2), dtype=torch.float32, device=device)
+        shape = (s.B, s.H, s.N, s.D)
+        self.qp, self.kp, self.vp, self.op = (torch.empty(shape, dtype=torch.bfloat16, device=device)
+                                              for _ in range(4))
+
+    def profile(self, q, k, v, idx):
+        return svg_profile_heads(q, k, v, self.s, self.scale, idx, self.cand, self.workspace,
+                                 self.choice, self.err)
+
+    def __call__(self, q, k, v, idx, out=None, lse=False):
+        s = self.s
+        self.profile(q, k, v, idx)
+        for x, y in ((q, self.qp), (k, self.kp), (v, self.vp)):
+            svg_permute(x, s, self.choice, inverse=False, out=y)
+        out, _, lse_t = svg_block_sparse_attn(q, k, v, s, self.scale, self.cand,
+                                              head_mask=self.choice, head_layout=self.choice,
+                                              qp=self.qp, kp=self.kp, vp=self.vp, out=out,
+                                              op=self.op, lse=lse)
+        svg_permute(self.op, s, self.choice, inverse=True, out=out)
+        return out, lse_t
+
+
+class StaticSparseAttention:
+    def __init__(self, s: Shape, dense_masks: torch.Tensor, repetitive: torch.Tensor = None,
+                 k_anchors: int = 5, scale: float = None):
+        """dense_masks: uint8 [H, nB, nB] (one mask per head); repetitive:
+        int32 [B*H] device flags of the row-repetitive heads (or None)."""
+        self.s = s
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(s.D)
+        self.k = k_anchors
+        self.repetitive = repetitive
+        masks = dense_masks.clone()
+        if repetitive is not None:
+            svg_restrict_anchor_rows(masks, s, repetitive[: masks.shape[0]].contiguous(), k_anchors)
+        self.masks = svg_encode_mask(masks)
+
+    def __call__(self, q, k, v, out=None, lse=False):
+        out, _, lse_t = svg_block_sparse_attn(q, k, v, self.s, self.scale, self.masks, out=out,
+                                              lse=lse)
+        if self.repetitive is not None:
+            svg_row_broadcast(out, self.s, self.repetitive, self.k)
+        return out, lse_t
+
+
+def kept_pairs_per_mask(masks: EncodedMasks, N: int, block: int) -> np.ndarray:
+    """(query, key) token pairs inside the kept blocks of each encoded mask,
+    counted from the skip list (tokens past N excluded).  int64 [n_masks]."""
+    rp = masks.row_ptr.cpu().numpy().astype(np.int64)
+    iv = masks.iv[: int(rp[-1])].cpu().numpy().astype(np.int64)
+    n_qb = masks.n_qb
+
+    def tokens_upto(c):  # tokens in key blocks [0, c)
+        return np.minimum(c * block, N)
+
+    per_iv = tokens_upto(iv[:, 1]) - tokens_upto(iv[:, 0]) if len(iv) else np.zeros(0, np.int64)
+    rows = np.repeat(np.arange(len(rp) - 1), np.diff(rp))
+    row_keys = np.bincount(rows, weights=per_iv, minlength=len(rp) - 1).astype(np.int64)
+    r = np.arange(n_qb)
+    q_tokens = np.minimum((r + 1) * block, N) - r * block
+    return (row_keys.reshape(masks.n_masks, n_qb) * q_tokens[None, :]).sum(axis=1)
+
+
+def attention_flops(masks: EncodedMasks, head_mask, N: int, block: int, D: int) -> int:
+    """Algorithmic FLOP of one block-sparse attention call: 4*D per kept
+    (query, key) pair (one multiply-add each for q.k and p.v per head dim)."""
+    pairs = kept_pairs_per_mask(masks, N, block)
+    return int(sum(4 * D * int(pairs[m]) for m in head_mask))

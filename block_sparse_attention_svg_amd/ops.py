@@ -1,0 +1,214 @@
+"""Python binding of the C ABI: one function per entry point, same names.
+
+Argument marshalling only (dtype / shape / device checks, raw pointers and
+torch's current stream); every step of the computation runs in libsvg's HIP
+kernels.  Tensors are torch CUDA tensors; PyTorch provides device memory and
+streams.
+"""
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass(frozen=True)
+class Shape:
+    B: int
+    H: int
+    N: int
+    D: int
+    F: int
+    Hs: int
+    Ws: int
+    block: int
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.N // self.block)
+
+    @property
+    def N_video(self) -> int:
+        return self.F * self.Hs * self.Ws
+
+    def c(self) -> L.SvgShape:
+        return L.SvgShape(self.B, self.H, self.N, self.D, self.F, self.Hs, self.Ws, self.block)
+
+
+@dataclass
+class EncodedMasks:
+    """Bitmap + skip list of n_masks block masks (device tensors)."""
+    n_masks: int
+    n_qb: int
+    n_kb: int
+    bitmap: torch.Tensor    # int32 view of uint32 words [n_masks, n_qb, ceil(n_kb/32)]
+    row_ptr: torch.Tensor   # int32 [n_masks*n_qb + 1]
+    iv: torch.Tensor        # int32 [capacity, 2]
+
+    def c(self) -> L.SvgMask:
+        return L.SvgMask(self.n_masks, self.n_qb, self.n_kb, self.bitmap.data_ptr(),
+                         self.row_ptr.data_ptr(), self.iv.data_ptr())
+
+    def n_intervals(self) -> int:
+        return int(self.row_ptr[-1].item())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_act(t, name, s: Shape, dtype=torch.bfloat16):
+    _need(t, name, dtype)
+    if tuple(t.shape) != (s.B, s.H, s.N, s.D):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(s.B, s.H, s.N, s.D)}")
+
+
+def svg_build_masks(s: Shape, band_w: int, out: torch.Tensor = None, device="cuda") -> torch.Tensor:
+    """Dense uint8 candidate masks [2, nB, nB]: [0] spatial, [1] temporal."""
+    nB = s.n_blocks
+    if out is None:
+        out = torch.empty((2, nB, nB), dtype=torch.uint8, device=device)
+    _need(out, "out", torch.uint8)
+    L.check("svg_build_masks", L.lib().svg_build_masks(s.c(), band_w, _ptr(out), _stream()))
+    return out
+
+
+def svg_encode_iv_capacity(n_masks: int, n_qb: int, n_kb: int) -> int:
+    return int(L.lib().svg_encode_iv_capacity(n_masks, n_qb, n_kb))
+
+
+def svg_encode_mask(dense: torch.Tensor) -> EncodedMasks:
+    """Encode dense uint8 masks [n_masks, n_qb, n_kb] into bitmap + skip list."""
+    _need(dense, "dense", torch.uint8)
+    if dense.dim() != 3:
+        raise ValueError("dense must be [n_masks, n_qb, n_kb]")
+    M, nq, nk = dense.shape
+    cap = svg_encode_iv_capacity(M, nq, nk)
+    dev = dense.device
+    bitmap = torch.empty((M, nq, -(-nk // 32)), dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(M * nq + 1, dtype=torch.int32, device=dev)
+    iv = torch.empty((max(cap, 1), 2), dtype=torch.int32, device=dev)
+    L.check("svg_encode_mask", L.lib().svg_encode_mask(
+        _ptr(dense), M, nq, nk, _ptr(bitmap), _ptr(row_ptr), _ptr(iv), cap, _stream()))
+    return EncodedMasks(M, nq, nk, bitmap, row_ptr, iv)
+
+
+def svg_permute(x: torch.Tensor, s: Shape, head_sel: torch.Tensor = None, inverse: bool = False,
+                out: torch.Tensor = None) -> torch.Tensor:
+    """Frame-major -> token-major (inverse=False) or back, for heads with head_sel != 0."""
+    dt = {torch.bfloat16: L.SVG_BF16, torch.float32: L.SVG_F32}.get(x.dtype)
+    if dt is None:
+        raise TypeError("x must be bfloat16 or float32")
+    _need_act(x, "x", s, x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    _need_act(out, "out", s, x.dtype)
+    if head_sel is not None:
+        _need(head_sel, "head_sel", torch.int32)
+    L.check("svg_permute", L.lib().svg_permute(_ptr(x), _ptr(out), dt, s.c(), _ptr(head_sel),
+                                               int(bool(inverse)), _stream()))
+    return out
+
+
+def svg_profile_workspace_bytes(s: Shape, n_samples: int) -> int:
+    return int(L.lib().svg_profile_workspace_bytes(s.c(), n_samples))
+
+
+def svg_profile_heads(q, k, v, s: Shape, scale: float, idx: torch.Tensor, cand: EncodedMasks,
+                      workspace: torch.Tensor = None, choice: torch.Tensor = None,
+                      err: torch.Tensor = None):
+    """Per-head mask choice (0 spatial, 1 temporal) and errors [B*H, 2]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need_act(t, n, s)
+    _need(idx, "idx", torch.int32)
+    ns = idx.numel()
+    need = svg_profile_workspace_bytes(s, ns)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if choice is None:
+        choice = torch.empty(s.B * s.H, dtype=torch.int32, device=q.device)
+    if err is None:
+        err = torch.empty((s.B * s.H, 2), dtype=torch.float32, device=q.device)
+    cm = cand.c()
+    L.check("svg_profile_heads", L.lib().svg_profile_heads(
+        _ptr(q), _ptr(k), _ptr(v), s.c(), float(scale), _ptr(idx), ns, ctypes.byref(cm),
+        _ptr(choice), _ptr(err), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream()))
+    return choice, err
+
+
+def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
+                          head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
+                          qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False):
+    """Block-sparse attention; returns (o, op, lse or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need_act(t, n, s)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_act(out, "out", s)
+    if head_layout is not None:
+        _need(head_layout, "head_layout", torch.int32)
+        for t, n in ((qp, "qp"), (kp, "kp"), (vp, "vp")):
+            _need_act(t, n, s)
+        if op is None:
+            op = torch.empty_like(q)
+        _need_act(op, "op", s)
+    if head_mask is not None:
+        _need(head_mask, "head_mask", torch.int32)
+    lse_t = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=q.device) if lse else None
+    mc = masks.c()
+    L.check("svg_block_sparse_attn", L.lib().svg_block_sparse_attn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), s.c(),
+        float(scale), ctypes.byref(mc), _ptr(head_mask), _ptr(head_layout), _ptr(lse_t),
+        _stream()))
+    return out, op, lse_t
+
+
+def svg_row_broadcast(o: torch.Tensor, s: Shape, head_sel: torch.Tensor, k_anchors: int):
+    _need_act(o, "o", s)
+    if head_sel is not None:
+        _need(head_sel, "head_sel", torch.int32)
+    L.check("svg_row_broadcast", L.lib().svg_row_broadcast(_ptr(o), s.c(), _ptr(head_sel),
+                                                           int(k_anchors), _stream()))
+    return o
+
+
+def svg_restrict_anchor_rows(masks: torch.Tensor, s: Shape, mask_sel: torch.Tensor, k_anchors: int):
+    _need(masks, "masks", torch.uint8)
+    if mask_sel is not None:
+        _need(mask_sel, "mask_sel", torch.int32)
+    L.check("svg_restrict_anchor_rows", L.lib().svg_restrict_anchor_rows(
+        _ptr(masks), masks.shape[0], s.c(), _ptr(mask_sel), int(k_anchors), _stream()))
+    return masks
+
+
+def svg_calibrate_masks(energy: torch.Tensor, eps: float, out: torch.Tensor = None) -> torch.Tensor:
+    """uint8 masks from float64 block energies [n_masks, n_qb, n_kb]."""
+    _need(energy, "energy", torch.float64)
+    M, nq, nk = energy.shape
+    if out is None:
+        out = torch.empty((M, nq, nk), dtype=torch.uint8, device=energy.device)
+    _need(out, "out", torch.uint8)
+    L.check("svg_calibrate_masks", L.lib().svg_calibrate_masks(
+        _ptr(energy), M, nq, nk, float(eps), _ptr(out), _stream()))
+    return out
+
+
+def svg_version() -> str:
+    return L.lib().svg_version().decode()

@@ -1,0 +1,197 @@
+/*
+ * svg.h - C ABI of block-sparse 3D attention for video diffusion transformers
+ *         (spatial / temporal heads, online head profiling, token-major layout,
+ *         calibrated static block masks), MI355X / gfx950.
+ *
+ * Sources named in the comments:
+ *   [SVG]      Sparse VideoGen article (m.jxzklqfsx.com/article/815093)
+ *   [CalibAtt] calibrated sparse attention article (lpnh.cn/news/568491)
+ *   [VDA]      video-diffusion acceleration survey (wmrh.cn/news/48564)
+ *   [SparsePR] SparsePR tutorial (lqnn.cn/news/72918)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Array pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *   unless a comment says "host".  The caller owns every buffer; the library
+ *   never allocates, frees or keeps a pointer after the call returns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call only enqueues work on `stream`; none synchronises with the host.
+ * - Activations are [B, H, N, D] row-major contiguous tensors ([SparsePR]
+ *   section 2.1 uses this layout; the output has the shape of dense attention
+ *   so it drops in for it).  Tokens are a video latent of F frames of Hs x Ws
+ *   positions stored frame-major (token f*Hs*Ws + y*Ws + x), followed by
+ *   N - F*Hs*Ws appended text tokens.
+ * - Return value: SVG_OK or an error code.  Arguments are validated on the host
+ *   before anything is enqueued; an invalid call enqueues nothing.  On error,
+ *   svg_last_error() returns a description (thread-local, valid until the next
+ *   call on the same thread).  SVG_ERR_HIP means a launch failed; its HIP
+ *   error string is in svg_last_error().
+ * - Device contents that violate a documented precondition (an out-of-range
+ *   mask index, a skip-list interval outside [0, n_kb)) are clamped or skipped
+ *   by the kernels, never dereferenced out of bounds, but give unspecified
+ *   numbers.
+ */
+#ifndef SVG_H
+#define SVG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVG_OK = 0,
+  SVG_ERR_INVALID_ARG = 1,  /* null pointer, bad size, aliasing, ...          */
+  SVG_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. head dim 96)    */
+  SVG_ERR_CAPACITY = 3,     /* an output or workspace buffer is too small      */
+  SVG_ERR_HIP = 4           /* a HIP launch or query failed                    */
+} svg_status;
+
+typedef enum { SVG_BF16 = 0, SVG_F32 = 1 } svg_dtype;
+
+/* Shape of one attention layer. */
+typedef struct {
+  int B, H, N, D;   /* batch, heads, tokens (video + text), head dim (64 or 128) */
+  int F, Hs, Ws;    /* latent frames and rows x columns per frame; F*Hs*Ws <= N */
+  int block;        /* query and key block edge: 64 or 128                      */
+} svg_shape;
+
+/* Encoded block masks ([CalibAtt] section 3.3: bitmap + skip list).
+ * bitmap : uint32 [n_masks][n_qb][ceil(n_kb/32)]; key block c of row r is bit
+ *          c%32 of word c/32 (LSB first); padding bits are 0.
+ * row_ptr: int32 [n_masks*n_qb + 1]; the intervals of row r of mask m are
+ *          iv[row_ptr[m*n_qb + r] .. row_ptr[m*n_qb + r + 1]).
+ * iv     : int32 pairs [start, end) of kept key blocks, ascending, disjoint,
+ *          maximal; empty rows have none. */
+typedef struct {
+  int n_masks, n_qb, n_kb;
+  const uint32_t* bitmap;
+  const int32_t* row_ptr;
+  const int32_t* iv;
+} svg_mask;
+
+/* ---- a1: per-shape candidate masks ------------------------------------- */
+/* Writes the dense uint8 masks [2][nB][nB] (nB = ceil(N/block)) of the two
+ * head types ([SVG], "Spatial Head" and "Temporal Head"):
+ *   [0] spatial, on frame-major blocks: a block pair is kept when some video
+ *       token of the query block and some video token of the key block are at
+ *       most one frame apart;
+ *   [1] temporal, on token-major blocks: kept when |r - c| <= band_w.
+ * On both, every key block holding a text token is kept in every row and every
+ * query block holding a text token keeps all key blocks.  Only s.N, s.F, s.Hs,
+ * s.Ws and s.block are read.  masks: device uint8, 2*nB*nB bytes. */
+svg_status svg_build_masks(svg_shape s, int band_w, uint8_t* masks, void* stream);
+
+/* ---- a2: mask encoding -------------------------------------------------- */
+/* Worst-case interval count of n_masks masks (rows alternate kept / skipped):
+ * n_masks * n_qb * ceil(n_kb/2).  Host function, no device work. */
+int64_t svg_encode_iv_capacity(int n_masks, int n_qb, int n_kb);
+
+/* Encodes dense uint8 masks [n_masks][n_qb][n_kb] (nonzero = keep) into the
+ * bitmap and skip list of svg_mask ([CalibAtt] section 3.3).  bitmap must hold
+ * n_masks*n_qb*ceil(n_kb/32) words, row_ptr n_masks*n_qb+1 entries and iv
+ * iv_capacity pairs; iv_capacity below svg_encode_iv_capacity(...) gives
+ * SVG_ERR_CAPACITY (the actual count is row_ptr[n_masks*n_qb], known on the
+ * device only).  Output is deterministic and identical on every call. */
+svg_status svg_encode_mask(const uint8_t* dense, int n_masks, int n_qb, int n_kb,
+                           uint32_t* bitmap, int32_t* row_ptr, int32_t* iv,
+                           int64_t iv_capacity, void* stream);
+
+/* ---- a4 / a6: layout permutation ---------------------------------------- */
+/* Frame-major <-> token-major transpose of selected heads ([SVG], "Layout
+ * Transformation + Kernel"): video token i = f*S + s (S = Hs*Ws) moves to
+ * p = s*F + f; text tokens keep their index.  inverse = 0: y[p(i)] = x[i]
+ * (frame -> token major); inverse = 1: y[i] = x[p(i)].  x, y: [B,H,N,D] of
+ * dtype dt, must not overlap.  head_sel: device int32 [B*H]; only heads with
+ * a nonzero entry are written, the rest of y is left untouched.  NULL selects
+ * every head.  Bit-exact data movement. */
+svg_status svg_permute(const void* x, void* y, svg_dtype dt, svg_shape s,
+                       const int32_t* head_sel, int inverse, void* stream);
+
+/* ---- a3: online head profiling ------------------------------------------ */
+/* Workspace size in bytes for svg_profile_heads (host function). */
+size_t svg_profile_workspace_bytes(svg_shape s, int n_samples);
+
+/* Picks each head's mask by sampled-query error ([SVG], online profiling:
+ * sample about 64 queries, compute their attention under the spatial and the
+ * temporal mask, compare each with dense attention, keep the smaller error).
+ *   q, k, v : bf16 [B,H,N,D] frame-major.
+ *   idx     : device int32 [n_samples], distinct frame-major video-token
+ *             indices (< F*Hs*Ws), shared by every head; 1 <= n_samples <= 64.
+ *   cand    : host struct, n_masks == 2, n_qb == n_kb == ceil(N/block):
+ *             [0] spatial on frame-major blocks, [1] temporal on token-major
+ *             blocks (only the bitmap is read).
+ *   choice  : device int32 [B*H] out: 0 spatial, 1 temporal (a tie -> 0).
+ *   err     : device float [B*H][2] out, or NULL: squared L2 error of the
+ *             spatial / temporal output against dense attention, summed over
+ *             the samples and the head dim (fp32, from the decomposition
+ *             o_dense - o_m = (Z_out/Z) (U_out/Z_out - U_in/Z_in)).
+ *   workspace: device, >= svg_profile_workspace_bytes(s, n_samples) bytes.
+ * Deterministic: fixed reduction order, identical results on every call. */
+svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_shape s,
+                             float scale, const int32_t* idx, int n_samples,
+                             const svg_mask* cand, int32_t* choice, float* err,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- a5: block-sparse attention ----------------------------------------- */
+/* Softmax attention restricted, per query block, to the key blocks of the
+ * head's mask row ([CalibAtt] sections 2.2 and 3.3; [VDA] section 2.1 for the
+ * attention itself, section 5.3 for tiled online softmax).  Only the kept
+ * blocks listed in the skip list are read.  Not causal.
+ *   q, k, v, o     : bf16 [B,H,N,D] frame-major.
+ *   qp, kp, vp, op : bf16 [B,H,N,D] token-major twins; may be NULL when no
+ *                    head uses layout 1.
+ *   masks          : host struct; n_qb == n_kb == ceil(N/block).
+ *   head_mask      : device int32 [B*H]: mask index of each head (clamped to
+ *                    [0, n_masks)); NULL means mask h % n_masks for head h.
+ *   head_layout    : device int32 [B*H]: 0 = attend q,k,v -> o; nonzero =
+ *                    attend qp,kp,vp -> op (mask blocks are then token-major
+ *                    blocks); NULL means all 0.
+ *   lse            : device float [B,H,N] out (natural-log log-sum-exp of the
+ *                    scaled logits, in the layout the head attends in), or NULL.
+ * A query block whose mask row is empty gets o = 0 and lse = -inf.
+ * bf16 inputs, fp32 accumulation and softmax, bf16 output. */
+svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
+                                 const void* qp, const void* kp, const void* vp, void* op,
+                                 svg_shape s, float scale, const svg_mask* masks,
+                                 const int32_t* head_mask, const int32_t* head_layout,
+                                 float* lse, void* stream);
+
+/* ---- a7: row-repetitive heads ------------------------------------------- */
+/* Anchor-row broadcast ([CalibAtt] section 3.2): in every frame, latent row y
+ * takes the output of its anchor row a(y) = floor((2j+1)*Hs/(2k)) with
+ * j = floor(y*k/Hs) (k equally spaced band centres).  o: bf16 [B,H,N,D]
+ * frame-major, rewritten in place for heads with head_sel != 0 (device int32
+ * [B*H]); text tokens untouched.  1 <= k_anchors <= Hs. */
+svg_status svg_row_broadcast(void* o, svg_shape s, const int32_t* head_sel, int k_anchors,
+                             void* stream);
+
+/* Empties, in place, the rows of dense uint8 masks [n_masks][nB][nB] whose
+ * frame-major query block holds no anchor-row video token, for masks with
+ * mask_sel != 0 (device int32 [n_masks]).  Attention then computes only the
+ * anchor-holding query blocks of a row-repetitive head ([CalibAtt] 3.2). */
+svg_status svg_restrict_anchor_rows(uint8_t* masks, int n_masks, svg_shape s,
+                                    const int32_t* mask_sel, int k_anchors, void* stream);
+
+/* ---- calibrated static masks -------------------------------------------- */
+/* Energy-threshold selection ([CalibAtt] section 3.1): for each row r of
+ * energies E [n_masks][n_qb][n_kb] (float64, >= 0), rank key blocks by energy
+ * (descending, ties by smaller index) and keep the shortest prefix whose
+ * running sum reaches eps * total; sums are taken in that order in float64,
+ * term by term, total being the last running sum.  out: uint8 masks of the
+ * same shape.  n_kb <= 4096; 0 < eps <= 1. */
+svg_status svg_calibrate_masks(const double* energy, int n_masks, int n_qb, int n_kb,
+                               double eps, uint8_t* out, void* stream);
+
+/* ---- errors -------------------------------------------------------------- */
+const char* svg_status_string(svg_status st);
+const char* svg_last_error(void);
+/* Library version string, e.g. "svg-mi355x 0.1 gfx950". */
+const char* svg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVG_H */

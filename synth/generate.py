@@ -19,6 +19,8 @@ default_rng(c*1000 + 500 + h); head classes from default_rng(c*31); the
 row-repetitive heads from default_rng(c*7 + 3).
 """
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -31,11 +33,11 @@ TEMPORAL = 1
 
 def head_classes(w: Workload) -> np.ndarray:
     """Generator class of every head (0 spatial, 1 temporal), int32 [H]."""
-    if w.name == "tiny":
-        return np.array([SPATIAL, TEMPORAL], dtype=np.int32)[: w.H]
+    if w.name == "tiny" and w.H == 2:
+        return np.array([SPATIAL, TEMPORAL], dtype=np.int32)
     perm = np.random.default_rng(w.seed * 31).permutation(w.H)
     cls = np.full(w.H, TEMPORAL, dtype=np.int32)
-    cls[perm[: w.n_spatial]] = SPATIAL
+    cls[perm[: min(w.n_spatial, w.H)]] = SPATIAL
     return cls
 
 
@@ -92,12 +94,18 @@ def gen_qkv(w: Workload, dtype: str = None, heads=None):
     cls = head_classes(w)
     heads = list(range(w.H)) if heads is None else list(heads)
     out = [torch.empty((w.B, len(heads), w.N, w.D), dtype=tdt) for _ in range(3)]
-    for b in range(w.B):
-        for j, h in enumerate(heads):
-            arrs = gen_head_qkv(w, h + b * w.H, int(cls[h]))
-            for t, a in zip(out, arrs):
-                a32 = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-                t[b, j] = a32.to(tdt)
+
+    def one(job):
+        b, j, h = job
+        arrs = gen_head_qkv(w, h + b * w.H, int(cls[h]))
+        for t, a in zip(out, arrs):
+            a32 = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+            t[b, j] = a32.to(tdt)
+
+    jobs = [(b, j, h) for b in range(w.B) for j, h in enumerate(heads)]
+    # heads are independent and NumPy releases the GIL in the bulk draws
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1, len(jobs))) as ex:
+        list(ex.map(one, jobs))
     return out[0], out[1], out[2], cls[heads]
 
 

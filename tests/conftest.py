@@ -25,3 +25,23 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+_INPUT_CACHE = {}
+
+
+@pytest.fixture(scope="session")
+def workload_inputs():
+    """Cached canonical inputs per workload name: (w, q, k, v, classes) on the CPU."""
+    import synth
+
+    def get(name, **kw):
+        key = (name, tuple(sorted(kw.items())))
+        if key not in _INPUT_CACHE:
+            w = synth.get_workload(name)
+            dtype = kw.get("dtype", "bf16")
+            q, k, v, cls = synth.gen_qkv(w, dtype=dtype)
+            _INPUT_CACHE[key] = (w, q, k, v, cls)
+        return _INPUT_CACHE[key]
+
+    return get

@@ -1,0 +1,148 @@
+"""The C ABI loads, exports every declared symbol and rejects bad arguments
+on the host, before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_svg_amd as svg
+from block_sparse_attention_svg_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svg.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libsvg.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svg_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L._SIGS), "binding signatures must cover the header exactly"
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert lib.svg_version().decode().startswith("svg-mi355x")
+    assert lib.svg_status_string(L.SVG_ERR_CAPACITY) == b"SVG_ERR_CAPACITY"
+
+
+def _shape(**kw):
+    d = dict(B=1, H=2, N=1024, D=64, F=4, Hs=16, Ws=16, block=64)
+    d.update(kw)
+    return L.SvgShape(*[d[k] for k in ("B", "H", "N", "D", "F", "Hs", "Ws", "block")])
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000000)
+
+
+def _err():
+    return L.lib().svg_last_error().decode()
+
+
+def test_build_masks_validation():
+    lib = L.lib()
+    assert lib.svg_build_masks(_shape(block=96), 1, FAKE, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_build_masks(_shape(N=1000), 1, FAKE, None) == L.SVG_ERR_INVALID_ARG
+    assert "exceeds N" in _err()
+    assert lib.svg_build_masks(_shape(), 1, None, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_build_masks(_shape(), -1, FAKE, None) == L.SVG_ERR_INVALID_ARG
+
+
+def test_encode_capacity():
+    lib = L.lib()
+    assert lib.svg_encode_iv_capacity(2, 591, 591) == 2 * 591 * 296
+    need = lib.svg_encode_iv_capacity(1, 3, 5)
+    st = lib.svg_encode_mask(FAKE, 1, 3, 5, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == L.SVG_ERR_CAPACITY and "below worst case" in _err()
+    assert lib.svg_encode_mask(None, 1, 3, 5, FAKE, FAKE, FAKE, need, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_encode_mask(FAKE, 0, 3, 5, FAKE, FAKE, FAKE, need, None) == L.SVG_ERR_INVALID_ARG
+
+
+def test_permute_validation():
+    lib = L.lib()
+    assert lib.svg_permute(FAKE, FAKE, L.SVG_BF16, _shape(), None, 0, None) == L.SVG_ERR_INVALID_ARG
+    assert "overlap" in _err()
+    assert lib.svg_permute(FAKE, FAKE2, L.SVG_BF16, _shape(D=96), None, 0, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_permute(FAKE, FAKE2, 7, _shape(), None, 0, None) == L.SVG_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x20000008)
+    assert lib.svg_permute(FAKE, odd, L.SVG_BF16, _shape(), None, 0, None) == L.SVG_ERR_INVALID_ARG
+
+
+def _mask(n_masks=2, n=16):
+    return L.SvgMask(n_masks, n, n, FAKE.value, FAKE.value, FAKE.value)
+
+
+def test_profile_validation():
+    lib = L.lib()
+    s = _shape()
+    ws = lib.svg_profile_workspace_bytes(s, 64)
+    assert ws > 0
+    m = _mask()
+    args = lambda **kw: [kw.get("q", FAKE), FAKE, FAKE, kw.get("s", s), kw.get("scale", 0.125), FAKE,
+                         kw.get("ns", 64), ctypes.byref(kw.get("m", m)), FAKE, None, FAKE,
+                         kw.get("ws", ws), None]
+    assert lib.svg_profile_heads(*args(ns=65)) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_profile_heads(*args(ns=0)) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_profile_heads(*args(ws=ws - 1)) == L.SVG_ERR_CAPACITY
+    assert lib.svg_profile_heads(*args(m=_mask(n_masks=3))) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_profile_heads(*args(m=_mask(n=17))) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_profile_heads(*args(q=None)) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_profile_heads(*args(scale=0.0)) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_profile_heads(*args(s=_shape(D=80))) == L.SVG_ERR_UNSUPPORTED
+
+
+def test_attention_validation():
+    lib = L.lib()
+    s = _shape()
+    m = _mask(n_masks=1)
+    base = [FAKE, FAKE2, ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000),
+            None, None, None, None, s, 0.125, ctypes.byref(m), None, None, None, None]
+    a = list(base); a[12] = FAKE           # head_layout without token-major twins
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(base); a[3] = FAKE            # o aliases q
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(base); a[8] = _shape(D=256)
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_UNSUPPORTED
+    bad = _mask(n_masks=1, n=8)
+    a = list(base); a[10] = ctypes.byref(bad)
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+
+
+def test_broadcast_calibrate_validation():
+    lib = L.lib()
+    assert lib.svg_row_broadcast(FAKE, _shape(), None, 0, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_row_broadcast(FAKE, _shape(), None, 17, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_restrict_anchor_rows(FAKE, 1, _shape(), None, 0, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_calibrate_masks(FAKE, 1, 4, 5000, 0.9, FAKE2, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_calibrate_masks(FAKE, 1, 4, 8, 0.0, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_calibrate_masks(FAKE, 1, 4, 8, 1.5, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+
+
+def test_python_binding_raises_on_error():
+    with pytest.raises(svg.SvgError) as e:
+        L.check("svg_build_masks", L.lib().svg_build_masks(_shape(block=96), 1, FAKE, None))
+    assert e.value.status == L.SVG_ERR_UNSUPPORTED
+
+
+def test_flop_count_from_skip_list():
+    """Host-side FLOP count of the bench from an encoded mask (CPU tensors)."""
+    import torch
+    from block_sparse_attention_svg_amd.layer import kept_pairs_per_mask
+    N, B = 150, 64   # 3 blocks, the last one 22 tokens
+    # mask 0 keeps (0,0) and (2,2); mask 1 keeps everything
+    rp = torch.tensor([0, 1, 1, 2, 3, 4, 5], dtype=torch.int32)
+    iv = torch.tensor([[0, 1], [2, 3], [0, 3], [0, 3], [0, 3]], dtype=torch.int32)
+    m = svg.EncodedMasks(2, 3, 3, torch.zeros(1), rp, iv)
+    pairs = kept_pairs_per_mask(m, N, B)
+    assert pairs.tolist() == [64 * 64 + 22 * 22, N * N]

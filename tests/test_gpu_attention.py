@@ -1,0 +1,163 @@
+"""GPU parity of block-sparse attention against the float64 oracle.
+
+Tolerance per head (bf16 in, fp32 accumulate, bf16 out): max-abs <= 2e-2 and
+relative L2 <= 5e-3; log-sum-exp within 1e-3.  Small workloads are compared on
+every row; full-size workloads run in the bench's launch configuration (the
+whole online layer) and are compared on sampled query blocks that include the
+ragged last block and, for HunyuanVideo, the mixed video/text block.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_svg_amd as svg
+import oracle as O
+import synth as S
+from parity_utils import banner, assert_attn_close, to_np, LSE_ABS
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def shape_of(w, H=None, block=None):
+    return svg.Shape(w.B, H or w.H, w.N, w.D, w.F, w.Hs, w.Ws, block or w.block)
+
+
+def _run_heads(w, q, k, v, masks_np, layout, block=None, lse=False):
+    """GPU attention where head h uses mask masks_np[h] in layout[h]."""
+    s = shape_of(w, q.shape[1], block)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    enc = svg.svg_encode_mask(torch.from_numpy(np.ascontiguousarray(masks_np)).to(DEV))
+    lay = torch.tensor(layout, dtype=torch.int32, device=DEV)
+    hm = torch.arange(len(layout), dtype=torch.int32, device=DEV)
+    qp, kp, vp = (svg.svg_permute(t, s, lay) for t in (qd, kd, vd))
+    o, op, lse_t = svg.svg_block_sparse_attn(qd, kd, vd, s, 1.0 / np.sqrt(w.D), enc, head_mask=hm,
+                                             head_layout=lay, qp=qp, kp=kp, vp=vp, lse=lse)
+    torch.cuda.synchronize()
+    return o, op, lse_t
+
+
+def test_tiny_all_rows_and_lse(workload_inputs):
+    w, q32, k32, v32, cls = workload_inputs("tiny", dtype="f32")
+    banner("attn tiny")
+    q, k, v = (t.to(torch.bfloat16) for t in (q32, k32, v32))   # bf16 copy, oracle on the same bits
+    cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+    o, op, lse = _run_heads(w, q, k, v, cand, [0, 1], lse=True)
+    p = O.token_major_index(w.F, w.Hs, w.Ws, w.N)
+    for h in range(2):
+        ref_o, ref_lse = O.head_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                          v[0, h].float().numpy(), cand[h], h, w.F, w.Hs, w.Ws,
+                                          w.block, w.scale)
+        got = to_np(o[0, h]) if h == 0 else to_np(op[0, h])[p]
+        assert_attn_close(got, ref_o, f"tiny head {h}")
+        lse_h = lse[0, h].cpu().numpy()
+        lse_fm = lse_h if h == 0 else lse_h[p]       # LSE is stored in the attended layout
+        assert np.max(np.abs(lse_fm - ref_lse)) < LSE_ABS
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_dense_mask_equals_dense_attention(block, workload_inputs):
+    w, q32, k32, v32, _ = workload_inputs("tiny", dtype="f32")
+    banner("attn dense", block)
+    q, k, v = (t.to(torch.bfloat16) for t in (q32, k32, v32))
+    nb = -(-w.N // block)
+    masks = np.ones((2, nb, nb), np.uint8)
+    o, _, _ = _run_heads(w, q, k, v, masks, [0, 0], block=block)
+    for h in range(2):
+        ref, _ = O.dense_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                   v[0, h].float().numpy(), w.scale)
+        assert_attn_close(to_np(o[0, h]), ref, f"dense h{h} block {block}")
+
+
+def test_ragged_partial_blocks_and_empty_rows():
+    """N not a multiple of the block; some mask rows empty (o = 0, lse = -inf)."""
+    banner("attn ragged/empty")
+    w = S.get_workload("tiny", F=3, Hs=10, Ws=10, text=37, H=3, D=128)   # N = 337, 3 blocks of 128
+    q, k, v, _ = S.gen_qkv(w, dtype="bf16")
+    s = shape_of(w, block=128)
+    rng = np.random.default_rng(2)
+    masks = (rng.random((3, 3, 3)) < 0.6).astype(np.uint8)
+    masks[:, :, 2] = 1
+    masks[1, 1] = 0                     # empty row
+    o, _, lse = _run_heads(w, q, k, v, masks, [0, 0, 0], block=128, lse=True)
+    for h in range(3):
+        ref, ref_lse = O.block_masked_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                                v[0, h].float().numpy(), masks[h], 128, w.scale)
+        assert_attn_close(to_np(o[0, h]), ref, f"ragged head {h}")
+        g = lse[0, h].cpu().numpy()
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isneginf(g), ~fin)
+        assert np.max(np.abs(g[fin] - ref_lse[fin])) < LSE_ABS
+    assert torch.all(o[0, 1, 128:256] == 0)
+
+
+@pytest.mark.parametrize("D,block", [(64, 64), (128, 64), (64, 128)])
+def test_head_dims_and_blocks(D, block):
+    banner("attn dims", D, block)
+    w = S.get_workload("cogvideox", H=4, D=D, F=3, n_spatial=2)       # N = 4050: 32 blocks of 128, ragged
+    q, k, v, cls = S.gen_qkv(w, dtype="bf16")
+    s_masks = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, block, 3)
+    masks = np.stack([s_masks[c] for c in cls])
+    o, op, _ = _run_heads(w, q, k, v, masks, cls.tolist(), block=block)
+    p = O.token_major_index(w.F, w.Hs, w.Ws, w.N)
+    for h in range(4):
+        ref, _ = O.head_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                  v[0, h].float().numpy(), masks[h], int(cls[h]), w.F, w.Hs, w.Ws,
+                                  block, w.scale)
+        got = to_np(o[0, h]) if cls[h] == 0 else to_np(op[0, h])[p]
+        assert_attn_close(got, ref, f"D{D} B{block} head {h}")
+
+
+def _layer_outputs(name, workload_inputs, t=0):
+    w, q, k, v, cls = workload_inputs(name)
+    s = shape_of(w)
+    layer = svg.OnlineSparseAttention(s, w.band_w)
+    idx = torch.from_numpy(S.sample_query_idx(w, t)).to(DEV)
+    o, _ = layer(q.to(DEV), k.to(DEV), v.to(DEV), idx)
+    torch.cuda.synchronize()
+    return w, q, k, v, cls, layer.choice.cpu().numpy(), o
+
+
+def test_online_layer_cogvideox_all_rows(workload_inputs):
+    banner("layer cogvideox")
+    w, q, k, v, cls, choice, o = _layer_outputs("cogvideox", workload_inputs)
+    assert np.array_equal(choice, cls)
+    cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+    for h in [0, 1, 2, 3, 21, 22, 46, 47]:
+        ref, _ = O.head_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                  v[0, h].float().numpy(), cand[choice[h]], int(choice[h]),
+                                  w.F, w.Hs, w.Ws, w.block, w.scale)
+        assert_attn_close(to_np(o[0, h]), ref, f"cog head {h}")
+
+
+@pytest.mark.parametrize("name", ["wan720p", "hunyuan720p"])
+def test_online_layer_full_size_sampled(name, workload_inputs):
+    """Full workload through the layer driver; sampled query blocks vs oracle."""
+    banner("layer full", name)
+    w, q, k, v, cls, choice, o = _layer_outputs(name, workload_inputs)
+    assert np.array_equal(choice, cls)
+    cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+    nB = w.n_blocks
+    rng = np.random.default_rng(5)
+    heads = [int(np.nonzero(cls == 0)[0][0]), int(np.nonzero(cls == 1)[0][0]),
+             int(rng.integers(w.H)), w.H - 1]
+    p = O.token_major_index(w.F, w.Hs, w.Ws, w.N)
+    for h in heads:
+        lay = int(choice[h])
+        qbs = sorted(set([0, nB - 3, nB - 2, nB - 1] + rng.integers(0, nB, 3).tolist()))
+        ref, _ = O.head_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                  v[0, h].float().numpy(), cand[lay], lay, w.F, w.Hs, w.Ws,
+                                  w.block, w.scale, qblocks=qbs)
+        rows = ~np.isnan(ref[:, 0])
+        assert rows.sum() > 0
+        assert_attn_close(to_np(o[0, h])[rows], ref[rows], f"{name} head {h} blocks {qbs}")
+
+
+def test_attention_is_deterministic(workload_inputs):
+    banner("attn determinism")
+    w, q32, k32, v32, _ = workload_inputs("tiny", dtype="f32")
+    q, k, v = (t.to(torch.bfloat16) for t in (q32, k32, v32))
+    cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+    o1, op1, _ = _run_heads(w, q, k, v, cand, [0, 1])
+    o2, op2, _ = _run_heads(w, q, k, v, cand, [0, 1])
+    assert torch.equal(o1[0, 0], o2[0, 0]) and torch.equal(op1[0, 1], op2[0, 1])
