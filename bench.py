@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of one block-sparse 3D attention layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan720p]
+
+A step is one pass of the whole hot path over one synthetic layer input:
+candidate-mask build and encoding, online head profiling on 64 sampled
+queries, forward permutation of q/k/v for the temporal heads, block-sparse
+attention, inverse permutation of the temporal heads' output (online
+workloads); block-sparse attention plus anchor-row broadcast (the static
+calibrated workload).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the effective TFLOP/s over the kept blocks
+for the whole step (algorithmic FLOP of the attention / step time); the
+attention kernel's own rate, per-call times and the roofline of the dominant
+kernel (HIP events on the launch stream) are reported beside it, together with
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s on kept blocks + ms/attention layer, Wan-720p shape, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_pmc_counters.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_svg_amd", "csrc", "attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan720p",
+                    choices=["tiny", "cogvideox", "wan720p", "hunyuan720p", "static_wan720p"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle sample (0 disables it)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain device copy of 1 GiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def describe(w):
+    return (f"{w.name}: 1 layer, B={w.B}, {w.H} heads, D={w.D}, {w.F}x{w.Hs}x{w.Ws}"
+            f"{' + %d text' % w.text if w.text else ''} = {w.N} tokens, bf16, block {w.block}")
+
+
+def file_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, q, k, v, classes, budget_s):
+    """fp64 oracle on a bounded sample: whole query blocks of one spatial and one
+    temporal head, processed until the time budget is spent."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    if w.mode == "static":
+        import synth
+        masks = {h: O.calibrate_mask(synth.energy_matrix(w, h), w.eps) for h in (0, 1)}
+        jobs = [(0, 0), (1, 0)]
+    else:
+        cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+        hs = int(np.nonzero(classes == 0)[0][0]) if (classes == 0).any() else 0
+        ht = int(np.nonzero(classes == 1)[0][0]) if (classes == 1).any() else hs
+        masks = {hs: cand[0], ht: cand[1]}
+        jobs = [(hs, 0), (ht, 1)]
+    sizes = np.array([min(w.N, (b + 1) * w.block) - b * w.block for b in range(w.n_blocks)])
+    rng = np.random.default_rng(17)
+    order = rng.permutation(w.n_blocks)
+    flops = 0
+    blocks = 0
+    prepared = []
+    for h, lay in jobs:
+        qh, kh, vh = (t[0, h].float().numpy().astype(np.float64) for t in (q, k, v))
+        if lay == 1:
+            qh, kh, vh = (O.to_token_major(t, w.F, w.Hs, w.Ws) for t in (qh, kh, vh))
+        prepared.append((qh, kh, vh, masks[h]))
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < budget_s and i < w.n_blocks:
+        r = int(order[i])
+        for qh, kh, vh, M in prepared:
+            O.block_masked_attention(qh, kh, vh, M, w.block, w.scale, qblocks=[r])
+            flops += 4 * w.D * int(sizes[r]) * int(sizes @ M[r].astype(np.int64))
+            blocks += 1
+        i += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle, {blocks} whole query blocks ({i} per head) of one "
+                       f"spatial and one temporal head, {flops / 1e9:.1f} GFLOP in {dt:.1f} s; "
+                       f"host has {os.cpu_count()} cores")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(heads shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import block_sparse_attention_svg_amd as svg
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    w = synth.get_workload(args.workload)
+    q_c, k_c, v_c, classes = synth.gen_qkv(w, dtype="bf16")
+    q, k, v = (t.to(dev) for t in (q_c, k_c, v_c))
+    s = svg.Shape(w.B, w.H, w.N, w.D, w.F, w.Hs, w.Ws, w.block)
+    scale = 1.0 / math.sqrt(w.D)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    if w.mode == "online":
+        layer = svg.OnlineSparseAttention(s, w.band_w, scale=scale, n_samples=w.n_samples)
+        n_idx = max(args.steps + args.warmup, 1)
+        idx = [torch.from_numpy(synth.sample_query_idx(w, t)).to(dev) for t in range(n_idx)]
+        names = ["masks", "profile", "permute", "attention", "unpermute"]
+    else:
+        E = torch.from_numpy(np.stack([synth.energy_matrix(w, h) for h in range(w.H)])).to(dev)
+        dense = svg.svg_calibrate_masks(E, w.eps)
+        del E
+        sel = np.zeros(w.B * w.H, np.int32)
+        sel[synth.repetitive_heads(w)] = 1
+        layer = svg.StaticSparseAttention(s, dense, torch.from_numpy(sel).to(dev), w.k_anchors, scale)
+        names = ["attention", "broadcast"]
+
+    def step(t, ev):
+        """One pass of the hot path; ev[i] records before call i (len(names)+1 events)."""
+        if w.mode == "online":
+            ev[0].record(stream)
+            dm = svg.svg_build_masks(s, w.band_w, out=layer.dense_masks)
+            layer.cand = svg.svg_encode_mask(dm)
+            ev[1].record(stream)
+            layer.profile(q, k, v, idx[t % len(idx)])
+            ev[2].record(stream)
+            for x, y in ((q, layer.qp), (k, layer.kp), (v, layer.vp)):
+                svg.svg_permute(x, s, layer.choice, inverse=False, out=y)
+            ev[3].record(stream)
+            svg.svg_block_sparse_attn(q, k, v, s, scale, layer.cand, head_mask=layer.choice,
+                                      head_layout=layer.choice, qp=layer.qp, kp=layer.kp,
+                                      vp=layer.vp, out=o, op=layer.op)
+            ev[4].record(stream)
+            svg.svg_permute(layer.op, s, layer.choice, inverse=True, out=o)
+            ev[5].record(stream)
+        else:
+            ev[0].record(stream)
+            svg.svg_block_sparse_attn(q, k, v, s, scale, layer.masks, out=o)
+            ev[1].record(stream)
+            svg.svg_row_broadcast(o, s, layer.repetitive, layer.k)
+            ev[2].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    for t in range(args.warmup):
+        step(t, mk())
+    torch.cuda.synchronize()
+
+    # algorithmic FLOP of the attention call (kept blocks of each head's mask)
+    if w.mode == "online":
+        head_mask = layer.choice.cpu().numpy().tolist()
+        flop = svg.attention_flops(layer.cand, head_mask, w.N, w.block, w.D)
+        n_temporal = int(sum(head_mask))
+    else:
+        flop = svg.attention_flops(layer.masks, list(range(w.H)), w.N, w.block, w.D)
+        n_temporal = 0
+
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for t in range(args.steps):
+        step(args.warmup + t, evs[t])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    attn_ms = per["attention"]
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        try:
+            pmc = json.load(open(PMC_FILE))
+            key = w.name
+            if pmc.get("attn_src_sha") == file_hash(ATTN_SRC) and key in pmc.get("workloads", {}):
+                traffic = pmc["workloads"][key]["hbm_bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; no model weights)",
+        "config": {"workload": describe(w), "heads_temporal": n_temporal,
+                   "heads_spatial": w.H - n_temporal, "profiler_samples": w.n_samples,
+                   "attention_gflop": round(flop / 1e9, 2)},
+        "ms_per_call": {n: round(v, 4) for n, v in per.items()},
+        "attention_tflops": round(achieved, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if w.mode == "online":
+        tensor_bytes = w.N * w.D * 2
+        moved = 2 * 3 * n_temporal * tensor_bytes            # read + write of q, k, v
+        out["permute_gbs"] = round(moved / (per["permute"] * 1e-3) / 1e9, 1)
+        out["permute_hbm_frac"] = round(out["permute_gbs"] / PEAK_HBM_GBS, 4)
+        kv_bytes = 2 * w.B * w.H * tensor_bytes
+        out["profile_gbs"] = round(kv_bytes / (per["profile"] * 1e-3) / 1e9, 1)
+        out["profile_share"] = round(per["profile"] / ms_step, 4)
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, classes, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
