@@ -157,13 +157,15 @@ def main():
             ev[3].record(stream)
             svg.svg_block_sparse_attn(q, k, v, s, scale, layer.cand, head_mask=layer.choice,
                                       head_layout=layer.choice, qp=layer.qp, kp=layer.kp,
-                                      vp=layer.vp, out=o, op=layer.op)
+                                      vp=layer.vp, out=o, op=layer.op,
+                                      workspace=layer.attn_workspace)
             ev[4].record(stream)
             svg.svg_permute(layer.op, s, layer.choice, inverse=True, out=o)
             ev[5].record(stream)
         else:
             ev[0].record(stream)
-            svg.svg_block_sparse_attn(q, k, v, s, scale, layer.masks, out=o)
+            svg.svg_block_sparse_attn(q, k, v, s, scale, layer.masks, out=o,
+                                      workspace=layer.attn_workspace)
             ev[1].record(stream)
             svg.svg_row_broadcast(o, s, layer.repetitive, layer.k)
             ev[2].record(stream)

@@ -8,15 +8,16 @@ behind the C ABI in include/svg.h.  This package is the thin Python binding.
 from .ops import (
     Shape, EncodedMasks,
     svg_build_masks, svg_encode_iv_capacity, svg_encode_mask, svg_permute,
-    svg_profile_workspace_bytes, svg_profile_heads, svg_block_sparse_attn,
-    svg_row_broadcast, svg_restrict_anchor_rows, svg_calibrate_masks, svg_version,
+    svg_profile_workspace_bytes, svg_profile_heads, svg_attn_workspace_bytes,
+    svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows, svg_calibrate_masks, svg_version,
 )
 from .layer import OnlineSparseAttention, StaticSparseAttention, attention_flops, kept_pairs_per_mask
 from ._lib import SvgError, LIB_PATH
 
 __all__ = [
     "Shape", "EncodedMasks", "svg_build_masks", "svg_encode_iv_capacity", "svg_encode_mask",
-    "svg_permute", "svg_profile_workspace_bytes", "svg_profile_heads", "svg_block_sparse_attn",
+    "svg_permute", "svg_profile_workspace_bytes", "svg_profile_heads", "svg_attn_workspace_bytes",
+    "svg_block_sparse_attn",
     "svg_row_broadcast", "svg_restrict_anchor_rows", "svg_calibrate_masks", "svg_version",
     "OnlineSparseAttention", "StaticSparseAttention", "attention_flops", "kept_pairs_per_mask",
     "SvgError", "LIB_PATH",

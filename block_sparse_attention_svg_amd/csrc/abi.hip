@@ -195,7 +195,7 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,
                                  const int32_t* head_mask, const int32_t* head_layout, float* lse,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "svg_block_sparse_attn";
   if (svg_status st = check_shape(s, fn)) return st;
   if (svg_status st = check_head_dim(s, fn)) return st;
@@ -207,6 +207,11 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
   size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
   if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
     return fail(SVG_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+  size_t need = attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SVG_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return fail(SVG_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.qp = qp; a.kp = kp; a.vp = vp; a.op = op;
@@ -221,8 +226,14 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
   a.BH = s.B * s.H;
   a.N = s.N; a.D = s.D; a.block = s.block;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.vt = workspace;
   launch_attn(a, as_stream(stream));
   return check_launch(fn);
+}
+
+size_t svg_attn_workspace_bytes(svg_shape s) {
+  if (check_shape(s, "svg_attn_workspace_bytes") != SVG_OK) return 0;
+  return attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block);
 }
 
 svg_status svg_row_broadcast(void* o, svg_shape s, const int32_t* head_sel, int k_anchors,

@@ -287,11 +287,11 @@ struct Cfg2 {
   static constexpr int BLK = 128;
   static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int CPR = D / 8;                  // 16-byte data chunks per row
+  static constexpr int CPR = D / 8;                  // 16-byte data chunks per K row
   static constexpr int KROW = CPR + 1;               // chunks per padded K row
-  static constexpr int VROW = CPR + 4;               // chunks per padded V row
+  static constexpr int VROW = BLK / 8 + 1;           // chunks per padded V^T row (one d, 128 keys)
   static constexpr int KCH = BLK * KROW;             // chunks of the K tile
-  static constexpr int VCH = BLK * VROW;             // chunks of the V tile
+  static constexpr int VCH = D * VROW;               // chunks of the V^T tile
   static constexpr int BUF_CH = KCH + VCH;           // chunks per buffer
   static constexpr int SEGS = (BUF_CH + 63) / 64;    // 1-KB load segments per buffer
   static constexpr int SEG_PER_WAVE = (SEGS + WAVES - 1) / WAVES;
@@ -315,28 +315,107 @@ __device__ __forceinline__ void cursor_start(RowCursor& c, const int32_t* __rest
   c.valid = next_block(iv, c.r1, nKB, c.t, c.kb, c.kend);
 }
 
-// Byte offset, inside one key block of K (or V) in global memory, of the chunk
-// this lane fills in load segment u; -1 for padding / past the buffer.  Bit 30
-// marks a V chunk.
 template <int D>
-__device__ __forceinline__ int seg_source(int u, int wave, int lane) {
+__device__ __forceinline__ void mfma_qk(const char* kb_lds, int k_lane, const bf16x8* qreg,
+                                        f32x16* sacc) {
   using C = Cfg2<D>;
-  const int seg = u * C::WAVES + wave;
-  const int p = seg * 64 + lane;
-  if (seg >= C::SEGS || p >= C::BUF_CH) return -1;
-  if (p < C::KCH) {
-    const int r = p / C::KROW, c = p % C::KROW;
-    return c < C::CPR ? (r * D + c * 8) * 2 : -1;
+  // K operands of contraction step kk+1 are fetched while step kk computes
+  uint4 cur[C::KT], nxt[C::KT];
+#pragma unroll
+  for (int kt = 0; kt < C::KT; ++kt) {
+    sacc[kt] = f32x16{};
+    cur[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + (kt * 32 * C::KROW) * 16);
   }
-  const int q = p - C::KCH;
-  const int r = q / C::VROW, c = q % C::VROW;
-  return c < C::CPR ? ((r * D + c * 8) * 2) | (1 << 30) : -1;
+#pragma unroll
+  for (int kk = 0; kk < C::DK; ++kk) {
+    if (kk + 1 < C::DK) {
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+        nxt[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + (kt * 32 * C::KROW + 2 * (kk + 1)) * 16);
+    }
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur[kt]), qreg[kk], sacc[kt], 0, 0, 0);
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) cur[kt] = nxt[kt];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf16x8* pb,
+                                        f32x16* oacc) {
+  using C = Cfg2<D>;
+  // V^T operands of key step s+1 are fetched while step s computes
+  uint4 cur[C::DT], nxt[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+    cur[dt] = *reinterpret_cast<const uint4*>(vb_lds + v_lane + (dt * 32 * C::VROW) * 16);
+#pragma unroll
+  for (int s = 0; s < C::PS; ++s) {
+    if (s + 1 < C::PS) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        nxt[dt] = *reinterpret_cast<const uint4*>(vb_lds + v_lane + (dt * 32 * C::VROW + 2 * (s + 1)) * 16);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur[dt]), pb[s], oacc[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) cur[dt] = nxt[dt];
+  }
+}
+
+// Online softmax of one 128-key block: S (raw logits) -> P (bf16), updating the
+// running max m (log2 units, moved only when the block max exceeds it by more
+// than 2^8), the lane's share of the denominator and, on a move, O.
+template <int D>
+__device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* oacc, float& m_run,
+                                              float& l_part, int key0, int N, int h, float c2) {
+  using C = Cfg2<D>;
+  if (key0 + C::BLK > N) {
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+        if (key >= N) sacc[kt][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+  mx = fmaxf(mx, shfl_xor_f(mx, 32)) * c2;
+  if (mx > m_run + kRescaleLog2) {
+    const float alpha = fast_exp2(m_run - mx);
+    l_part *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+    m_run = mx;
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int s = 0; s < C::PS; ++s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pb[s][i] = (__bf16)fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + i], c2, -m_run));
+    // denominator from the same bf16 weights the PV product uses
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const bf16x2 pair = {pb[s][i], pb[s][i + 1]};
+      l_part = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_part, false);
+    }
+  }
 }
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pairs, int pairs_per_xcd) {
   using C = Cfg2<D>;
-  __shared__ uint4 lds[2][C::SEGS * 64];   // [buffer][K tile | V tile], padded rows
+  constexpr int KBYTES = C::KCH * 16, VBYTES = C::VCH * 16;
+  __shared__ uint4 lds[(2 * C::KCH + 2 * C::VCH)];   // K buffers 0,1 then V buffers 0,1
+  char* lds_b = reinterpret_cast<char*>(lds);
 
   // XCD-aware order: workgroup i runs on XCD i % 8; XCD x takes, head after
   // head, the x-th contiguous eighth of that head's query-block pairs.
@@ -348,10 +427,10 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
+  const int grp = wave >> 2;
   const int n = lane & 31, h = lane >> 5;
   const int N = a.N;
   const int qb0 = 2 * pair;
-  const int my_qb = qb0 + (wave >> 2);
   const bool has_b = qb0 + 1 < a.n_qb;
 
   int mask_id = a.head_mask ? a.head_mask[bh] : bh % a.n_masks;
@@ -360,10 +439,9 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   const int64_t head_off = int64_t(bh) * N * D;
   const __bf16* Q = static_cast<const __bf16*>(tm ? a.qp : a.q) + head_off;
   const char* Kh = reinterpret_cast<const char*>(static_cast<const __bf16*>(tm ? a.kp : a.k) + head_off);
-  const char* Vh = reinterpret_cast<const char*>(static_cast<const __bf16*>(tm ? a.vp : a.v) + head_off);
-  __bf16* O = static_cast<__bf16*>(tm ? a.op : a.o) + head_off;
+    __bf16* O = static_cast<__bf16*>(tm ? a.op : a.o) + head_off;
 
-  const int q_row = my_qb * C::BLK + (wave & 3) * 32 + n;
+  const int q_row = (qb0 + grp) * C::BLK + (wave & 3) * 32 + n;
   bf16x8 qreg[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
@@ -372,136 +450,135 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
     qreg[kk] = as_bf16x8(u);
   }
 
-  int src[C::SEG_PER_WAVE];
+  // This thread's share of the 16-byte global->LDS copies of one key block:
+  // K chunks first, then V chunks, 1 KB per wavefront instruction; lanes on
+  // row padding stay idle.  Source offset inside the block (bytes) or -1.
+  constexpr int KSEG = (C::KCH + 63) / 64, VSEG = (C::VCH + 63) / 64;
+  constexpr int KPW = (KSEG + C::WAVES - 1) / C::WAVES, VPW = (VSEG + C::WAVES - 1) / C::WAVES;
+  int ksrc[KPW], vsrc[VPW];
 #pragma unroll
-  for (int u = 0; u < C::SEG_PER_WAVE; ++u) src[u] = seg_source<D>(u, wave, lane);
-
-  // Stage key block kb into buffer b.  Keys past N (ragged last block) read
-  // row N-1 instead: finite values whose scores are masked to -inf.
-  auto stage = [&](int kb, int b) {
-    const int64_t blk_off = int64_t(kb) * C::BLK * D * 2;
-    const bool ragged = (kb + 1) * C::BLK > N;
+  for (int u = 0; u < KPW; ++u) {
+    const int p = (u * C::WAVES + wave) * 64 + lane;
+    const int r = p / C::KROW, c = p % C::KROW;
+    ksrc[u] = (p < C::KCH && c < C::CPR) ? (r * D + c * 8) * 2 : -1;
+  }
 #pragma unroll
-    for (int u = 0; u < C::SEG_PER_WAVE; ++u) {
+  for (int u = 0; u < VPW; ++u) {
+    const int p = (u * C::WAVES + wave) * 64 + lane;
+    const int r = p / C::VROW, c = p % C::VROW;
+    vsrc[u] = (p < C::VCH && c < C::BLK / 8) ? (r * C::BLK + c * 8) * 2 : -1;
+  }
+  // Keys past N (ragged last block) read row N-1 instead: finite values whose
+  // scores are masked to -inf and whose P weights are 0.
+  auto load_k = [&](int kb, char* dst) {
+    const char* blk = Kh + int64_t(kb) * C::BLK * D * 2;
+    const int last = N - 1 - kb * C::BLK;   // last valid row of this block
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) {
       const int seg = u * C::WAVES + wave;
-      if (seg < C::SEGS && src[u] >= 0) {
-        int off = src[u] & ~(1 << 30);
-        const char* base = (src[u] & (1 << 30)) ? Vh : Kh;
-        if (ragged) {
-          const int r = off / (D * 2);
-          const int last = N - 1 - kb * C::BLK;
-          if (r > last) off += (last - r) * D * 2;
-        }
-        __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + blk_off + off),
-                                         (LDS_AS void*)(&lds[b][seg * 64]), 16, 0, 0);
+      int off = ksrc[u];
+      if (seg < KSEG && off >= 0) {
+        const int r = off / (D * 2);
+        if (r > last) off += (last - r) * D * 2;
+        __builtin_amdgcn_global_load_lds((GLB_AS void*)(blk + off), (LDS_AS void*)(dst + seg * 1024),
+                                         16, 0, 0);
       }
+    }
+  };
+  // V^T tiles come from the block-transposed workspace: [D][128] per block,
+  // keys past N already zero
+  const char* Vt = static_cast<const char*>(a.vt) + int64_t(bh) * a.n_kb * C::BLK * D * 2;
+  auto load_v = [&](int kb, char* dst) {
+    const char* blk = Vt + int64_t(kb) * C::BLK * D * 2;
+#pragma unroll
+    for (int u = 0; u < VPW; ++u) {
+      const int seg = u * C::WAVES + wave;
+      if (seg < VSEG && vsrc[u] >= 0)
+        __builtin_amdgcn_global_load_lds((GLB_AS void*)(blk + vsrc[u]),
+                                         (LDS_AS void*)(dst + seg * 1024), 16, 0, 0);
     }
   };
 
   f32x16 oacc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled logits (log2 units), possibly stale by < 2^8
+  float m_run = -INFINITY;
   float l_part = 0.f;
+  f32x16 sacc[C::KT];
+  bf16x8 pb[C::PS];
 
   RowCursor ca, cb;
   cursor_start(ca, a.row_ptr, a.iv, mask_id * a.n_qb + qb0, true, a.n_kb);
   cursor_start(cb, a.row_ptr, a.iv, mask_id * a.n_qb + qb0 + 1, has_b, a.n_kb);
-  auto pick = [&](int& kb, bool& in_a, bool& in_b) -> bool {
+  // merged block sequence of the two rows; `mine` = the block is in my row
+  auto pick = [&](int& kb, bool& mine) -> bool {
     if (!ca.valid && !cb.valid) return false;
     kb = min(ca.valid ? ca.kb : INT_MAX, cb.valid ? cb.kb : INT_MAX);
-    in_a = ca.valid && ca.kb == kb;
-    in_b = cb.valid && cb.kb == kb;
+    const bool in_a = ca.valid && ca.kb == kb;
+    const bool in_b = cb.valid && cb.kb == kb;
     if (in_a) ca.valid = next_block(a.iv, ca.r1, a.n_kb, ca.t, ca.kb, ca.kend);
     if (in_b) cb.valid = next_block(a.iv, cb.r1, a.n_kb, cb.t, cb.kb, cb.kend);
+    mine = grp == 0 ? in_a : in_b;
     return true;
   };
 
-  int kb = 0;
-  bool in_a = false, in_b = false;
-  bool valid = pick(kb, in_a, in_b);
-  if (valid) stage(kb, 0);
-
   const int srow = swap_bits23(n);
   const float c2 = a.scale_log2;
-  // per-lane LDS byte offsets inside a buffer; everything else is immediate
   const int k_lane = (srow * C::KROW + h) * 16;
-  const int v_lane = C::KCH * 16 + ((8 * h + ((lane >> 2) & 3)) * C::VROW) * 16 +
-                     (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
-  int buf = 0;
-  while (valid) {
-    int nkb = 0;
-    bool nin_a = false, nin_b = false;
-    const bool nvalid = pick(nkb, nin_a, nin_b);
-    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's tile loads have landed
-    __syncthreads();                      // everyone's have, and buffer buf^1 is free
-    if (nvalid) stage(nkb, buf ^ 1);
+  const int v_lane = (n * C::VROW + h) * 16;   // V^T row d = n (+32*dt), keys 8h.. (+16s)
 
-    const bool mine = (wave < 4) ? in_a : in_b;
-    if (mine) {
-      const char* lb = reinterpret_cast<const char*>(lds[buf]);
-      // ---- S^T = K Q^T ----------------------------------------------------
-      f32x16 sacc[C::KT];
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt) {
-        sacc[kt] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < C::DK; ++kk) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(lb + k_lane + (kt * 32 * C::KROW + 2 * kk) * 16);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(raw), qreg[kk], sacc[kt], 0, 0, 0);
-        }
-      }
-      // ---- online softmax on raw logits; scale folded into the exponent ----
-      const int key0 = kb * C::BLK;
-      if (key0 + C::BLK > N) {
-#pragma unroll
-        for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-            if (key >= N) sacc[kt][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 32)) * c2;
-      if (mx > m_run + kRescaleLog2) {
-        const float alpha = fast_exp2(m_run - mx);
-        l_part *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
-        m_run = mx;
-      }
-      bf16x8 pb[C::PS];
-#pragma unroll
-      for (int s = 0; s < C::PS; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + i], c2, -m_run));
-          l_part += p;
-          pb[s][i] = (__bf16)p;
-        }
-      // ---- O^T += V^T P^T; V^T operand by transposing LDS reads -------------
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-        for (int s = 0; s < C::PS; ++s) {
-          const char* p0 = lb + v_lane + (16 * s * C::VROW) * 16 + dt * 64;
-          bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
-          bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 4 * C::VROW * 16));
-          bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[s], oacc[dt], 0, 0, 0);
-        }
-      }
+  // cur: block j (K_j staged / being used); prev: block j-1 (V_{j-1})
+  int kb_cur = 0, kb_prev = 0;
+  bool mine_cur = false, mine_prev = false;
+  bool have_cur = pick(kb_cur, mine_cur);
+  bool have_prev = false;
+  if (have_cur) load_k(kb_cur, lds_b);
+  __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+  __syncthreads();
+
+  int j = 0;
+  while (have_cur || have_prev) {
+    const int kbuf = j & 1;
+    char* k_cur = lds_b + kbuf * KBYTES;
+    char* v_prev = lds_b + 2 * KBYTES + (kbuf ^ 1) * VBYTES;
+    // loads for the next iteration: K_{j+1}, V_j
+    int kb_next = 0;
+    bool mine_next = false;
+    const bool have_next = have_cur && pick(kb_next, mine_next);
+    if (have_next) load_k(kb_next, lds_b + (kbuf ^ 1) * KBYTES);
+    if (have_cur) load_v(kb_cur, lds_b + 2 * KBYTES + kbuf * VBYTES);
+
+    // ---- phase 1 --------------------------------------------------------------
+    if (grp == 0) {
+      if (have_prev && mine_prev) mfma_pv<D>(v_prev, v_lane, pb, oacc);
+      if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
+    } else {
+      if (have_prev && mine_prev)
+        softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_prev * C::BLK, N, h, c2);
     }
-    kb = nkb;
-    in_a = nin_a;
-    in_b = nin_b;
-    valid = nvalid;
-    buf ^= 1;
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase 2 --------------------------------------------------------------
+    if (grp == 0) {
+      if (have_cur && mine_cur)
+        softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_cur * C::BLK, N, h, c2);
+    } else {
+      if (have_prev && mine_prev) mfma_pv<D>(v_prev, v_lane, pb, oacc);
+      if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's loads have landed
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    kb_prev = kb_cur;
+    mine_prev = mine_cur;
+    have_prev = have_cur;
+    kb_cur = kb_next;
+    mine_cur = mine_next;
+    have_cur = have_next;
+    ++j;
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -515,7 +592,7 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
       for (int g = 0; g < 4; ++g) {
         bf16x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[dt][4 * g + j] * inv);
+        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(oacc[dt][4 * g + jj] * inv);
         *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * h) = w;
       }
     }
@@ -526,6 +603,35 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   }
 }
 
+// V of every head, transposed per 128-key block into the workspace
+// ([bh][kb][d][128], keys past N zero), so the attention kernel can stage V^T
+// tiles with plain 16-byte copies and read the PV operand with ds_read_b128.
+// One workgroup per (key block, head); each thread transposes 8 keys x 8 dims
+// in registers.  Heads with layout 1 read the token-major twin.
+template <int D>
+__global__ __launch_bounds__(256) void vt_prep_kernel(const __bf16* __restrict__ v,
+                                                      const __bf16* __restrict__ vp,
+                                                      const int32_t* __restrict__ head_layout,
+                                                      __bf16* __restrict__ vt, int N, int nKB) {
+  constexpr int BLK = 128, CPR = D / 8, TASKS = (BLK / 8) * CPR;
+  const int kb = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x;
+  if (t >= TASKS) return;
+  const bool tm = head_layout && head_layout[bh] != 0;
+  const uint4* src = reinterpret_cast<const uint4*>((tm ? vp : v) + int64_t(bh) * N * D);
+  const int dc = t % CPR, kg = t / CPR;
+  uint4 rows[8], cols[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = kb * BLK + 8 * kg + i;
+    rows[i] = key < N ? src[int64_t(key) * CPR + dc] : make_uint4(0, 0, 0, 0);
+  }
+  transpose8x8(rows, cols);
+  uint4* dst = reinterpret_cast<uint4*>(vt + (int64_t(bh) * nKB + kb) * BLK * D);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dst[(8 * dc + j) * (BLK / 8) + kg] = cols[j];
+}
+
 template <int D, int BLK>
 void launch_t(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.n_qb, a.BH);
@@ -534,6 +640,9 @@ void launch_t(const AttnArgs& a, hipStream_t st) {
 
 template <int D>
 void launch_b128(const AttnArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((vt_prep_kernel<D>), dim3(a.n_kb, a.BH), dim3(256), 0, st,
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.vp),
+                     a.head_layout, static_cast<__bf16*>(a.vt), a.N, a.n_kb);
   const int pairs = (a.n_qb + 1) / 2;
   const int per_xcd = (pairs + 7) / 8;
   dim3 grid(8 * per_xcd * a.BH);
@@ -541,6 +650,11 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t attn_workspace_bytes(int BH, int N, int D, int block) {
+  if (block != 128) return 0;
+  return size_t(BH) * ceil_div(N, 128) * 128 * D * 2;
+}
 
 void launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.block == 128) {

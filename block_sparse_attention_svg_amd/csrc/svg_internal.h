@@ -60,7 +60,9 @@ struct AttnArgs {
   float* lse;
   int BH, N, D, block;
   float scale_log2;  // softmax scale times log2(e)
+  void* vt;          // workspace: V of every head, block-transposed (128-key blocks)
 };
+size_t attn_workspace_bytes(int BH, int N, int D, int block);
 void launch_attn(const AttnArgs& a, hipStream_t st);
 
 struct ProfileArgs {

@@ -17,8 +17,8 @@ import numpy as np
 import torch
 
 from .ops import (Shape, EncodedMasks, svg_build_masks, svg_encode_mask, svg_permute,
-                  svg_profile_workspace_bytes, svg_profile_heads, svg_block_sparse_attn,
-                  svg_row_broadcast, svg_restrict_anchor_rows)
+                  svg_profile_workspace_bytes, svg_profile_heads, svg_attn_workspace_bytes,
+                  svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows)
 
 
 class OnlineSparseAttention:
@@ -36,6 +36,8 @@ class OnlineSparseAttention:
         shape = (s.B, s.H, s.N, s.D)
         self.qp, self.kp, self.vp, self.op = (torch.empty(shape, dtype=torch.bfloat16, device=device)
                                               for _ in range(4))
+        self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s), 1), dtype=torch.uint8,
+                                          device=device)
 
     def profile(self, q, k, v, idx):
         return svg_profile_heads(q, k, v, self.s, self.scale, idx, self.cand, self.workspace,
@@ -49,7 +51,7 @@ class OnlineSparseAttention:
         out, _, lse_t = svg_block_sparse_attn(q, k, v, s, self.scale, self.cand,
                                               head_mask=self.choice, head_layout=self.choice,
                                               qp=self.qp, kp=self.kp, vp=self.vp, out=out,
-                                              op=self.op, lse=lse)
+                                              op=self.op, lse=lse, workspace=self.attn_workspace)
         svg_permute(self.op, s, self.choice, inverse=True, out=out)
         return out, lse_t
 
@@ -67,10 +69,12 @@ class StaticSparseAttention:
         if repetitive is not None:
             svg_restrict_anchor_rows(masks, s, repetitive[: masks.shape[0]].contiguous(), k_anchors)
         self.masks = svg_encode_mask(masks)
+        self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s), 1), dtype=torch.uint8,
+                                          device=dense_masks.device)
 
     def __call__(self, q, k, v, out=None, lse=False):
         out, _, lse_t = svg_block_sparse_attn(q, k, v, self.s, self.scale, self.masks, out=out,
-                                              lse=lse)
+                                              lse=lse, workspace=self.attn_workspace)
         if self.repetitive is not None:
             svg_row_broadcast(out, self.s, self.repetitive, self.k)
         return out, lse_t

@@ -153,9 +153,14 @@ def svg_profile_heads(q, k, v, s: Shape, scale: float, idx: torch.Tensor, cand: 
     return choice, err
 
 
+def svg_attn_workspace_bytes(s: Shape) -> int:
+    return int(L.lib().svg_attn_workspace_bytes(s.c()))
+
+
 def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
                           head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
-                          qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False):
+                          qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False,
+                          workspace: torch.Tensor = None):
     """Block-sparse attention; returns (o, op, lse or None)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need_act(t, n, s)
@@ -172,11 +177,15 @@ def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
     if head_mask is not None:
         _need(head_mask, "head_mask", torch.int32)
     lse_t = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=q.device) if lse else None
+    need = svg_attn_workspace_bytes(s)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mc = masks.c()
     L.check("svg_block_sparse_attn", L.lib().svg_block_sparse_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), s.c(),
         float(scale), ctypes.byref(mc), _ptr(head_mask), _ptr(head_layout), _ptr(lse_t),
-        _stream()))
+        _ptr(workspace), ws_bytes, _stream()))
     return out, op, lse_t
 
 

@@ -151,13 +151,22 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  *                    blocks); NULL means all 0.
  *   lse            : device float [B,H,N] out (natural-log log-sum-exp of the
  *                    scaled logits, in the layout the head attends in), or NULL.
- * A query block whose mask row is empty gets o = 0 and lse = -inf.
+ *   workspace      : device scratch of >= svg_attn_workspace_bytes(s) bytes
+ *                    (V re-laid out per key block); may be NULL when that is 0.
+ * A query block whose mask row is empty gets o = 0 and lse = -inf.  The
+ * softmax denominator sums the same bf16-rounded weights as the PV product.
  * bf16 inputs, fp32 accumulation and softmax, bf16 output. */
 svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,
                                  const int32_t* head_mask, const int32_t* head_layout,
-                                 float* lse, void* stream);
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Workspace bytes svg_block_sparse_attn needs for shape s (host function):
+ * B*H*ceil(N/128)*128*D*2 for 128-token blocks (V transposed per key block),
+ * 0 for 64-token blocks. */
+size_t svg_attn_workspace_bytes(svg_shape s);
 
 /* ---- a7: row-repetitive heads ------------------------------------------- */
 /* Anchor-row broadcast ([CalibAtt] section 3.2): in every frame, latent row y

@@ -107,7 +107,7 @@ def test_attention_validation():
     s = _shape()
     m = _mask(n_masks=1)
     base = [FAKE, FAKE2, ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000),
-            None, None, None, None, s, 0.125, ctypes.byref(m), None, None, None, None]
+            None, None, None, None, s, 0.125, ctypes.byref(m), None, None, None, None, 0, None]
     a = list(base); a[12] = FAKE           # head_layout without token-major twins
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
     a = list(base); a[3] = FAKE            # o aliases q
@@ -117,6 +117,14 @@ def test_attention_validation():
     bad = _mask(n_masks=1, n=8)
     a = list(base); a[10] = ctypes.byref(bad)
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+    # 128-token blocks need a workspace of B*H*ceil(N/128)*128*D*2 bytes
+    s128 = _shape(block=128)
+    need = lib.svg_attn_workspace_bytes(s128)
+    assert need == 1 * 2 * 8 * 128 * 64 * 2
+    assert lib.svg_attn_workspace_bytes(_shape()) == 0
+    m128 = L.SvgMask(1, 8, 8, FAKE.value, FAKE.value, FAKE.value)
+    a = list(base); a[8] = s128; a[10] = ctypes.byref(m128); a[14] = ctypes.c_void_p(0x50000000); a[15] = need - 1
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_CAPACITY
 
 
 def test_broadcast_calibrate_validation():

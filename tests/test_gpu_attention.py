@@ -1,7 +1,7 @@
 """GPU parity of block-sparse attention against the float64 oracle.
 
 Tolerance per head (bf16 in, fp32 accumulate, bf16 out): max-abs <= 2e-2 and
-relative L2 <= 5e-3; log-sum-exp within 1e-3.  Small workloads are compared on
+relative L2 <= 5e-3; log-sum-exp within 2.5e-3 (bf16 weights in the denominator).  Small workloads are compared on
 every row; full-size workloads run in the bench's launch configuration (the
 whole online layer) and are compared on sampled query blocks that include the
 ragged last block and, for HunyuanVideo, the mixed video/text block.
