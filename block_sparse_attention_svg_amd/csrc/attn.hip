@@ -23,6 +23,8 @@
 // makes register r of a 32-key tile hold key 16*(r/8) + 8*(l/32) + r%8: the
 // eight keys a lane needs as its P^T operand for one PV step are then its
 // own registers, and the matching V^T operand is one 16-byte LDS read.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "svg_internal.h"
 
@@ -264,102 +266,193 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_fwd_kernel(AttnArgs a) {
 //
 // Both query blocks (rows r and r+1 of the head's mask) share every staged
 // key block; the workgroup walks the union of the two rows' skip lists and a
-// wavefront skips the MFMA work of blocks its own row does not keep.  K and V
-// land in double-buffered LDS through 16-byte global->LDS loads
-// (global_load_lds_dwordx4): block j+1 streams in while block j is computed,
-// and no registers hold staged data, so two wavefronts fit per SIMD and one's
-// softmax overlaps the other's MFMA.  V stays row-major in LDS; the V^T
-// operand of the PV product comes from ds_read_b64_tr_b16, which hands each
-// lane one column of a 4-row x 16-column tile.
+// wavefront skips the MFMA work of blocks its own row does not keep.  Waves
+// 0-3 (group 0) own the 128 queries of block r, waves 4-7 (group 1) those of
+// block r+1, 32 queries per wave, two waves per SIMD.
 //
-// LDS rows are padded so that every operand fetch is bank-conflict free and
-// every per-lane LDS address is a fixed base plus a compile-time offset:
-// K rows take D+8 elements (16 rows of one 16-byte fetch land on distinct
-// banks), V rows D+32 (4 rows x 64 bytes of a transposing fetch do).  The
-// global->LDS loads write 1 KB per wavefront instruction; lanes that fall on
-// padding stay idle.
+// Each key block j passes through two phases.  Phase 1: group 0 runs the
+// MFMAs (O += P_{j-1} V_{j-1}, S_j = Q K_j^T) while group 1 runs the softmax
+// of S_{j-1}; phase 2 swaps the roles.  The two waves sharing a SIMD thus
+// alternate between matrix work and VALU work.  K_j and V^T_j land in
+// double-buffered LDS through 16-byte global->LDS copies issued by the group
+// doing softmax: V^T of block j in phase 1 (group 1), K of block j+1 in
+// phase 2 (group 0).  The copies go out before that group's softmax and land
+// while the phase runs; the waves running MFMAs never issue one.  V^T comes
+// from a per-block transposed workspace, so both operands are read with
+// plain 16-byte LDS fetches.
 // ---------------------------------------------------------------------------
 #define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
+
+// A byte range of global memory as a buffer resource, for 16-byte
+// global->LDS copies (buffer_load_dwordx4 ... lds): lane offsets are 32-bit
+// VGPRs, a wave-uniform offset goes in an SGPR, the range check drops reads
+// past the end (nothing is fetched for them), and the LDS destination of the
+// wavefront instruction is the M0 base (lane l writes 16 bytes at base + 16 l).
+struct LdsCopySrc {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r;
+#endif
+  __device__ __forceinline__ LdsCopySrc(const void* base, int bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+#endif
+  }
+  __device__ __forceinline__ void copy16(uint32_t lane_off, uint32_t uniform_off, uint32_t lds_addr) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(uintptr_t)lds_addr, 16, lane_off,
+                                             uniform_off, 0, 0);
+#endif
+  }
+};
+
+// Scalar add of a compile-time constant, kept at its point of use: the
+// per-copy offsets are loop-invariant, and hoisted out of the loop all
+// together they would exceed the scalar registers and be spilled.
+template <int C>
+__device__ __forceinline__ uint32_t sadd(uint32_t a) {
+  uint32_t r;
+  asm volatile("s_add_u32 %0, %1, %2" : "=s"(r) : "s"(a), "i"(C) : "scc");
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(LDS_AS const void*)p;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
+}
 
 template <int D>
 struct Cfg2 {
   static constexpr int BLK = 128;
   static constexpr int WAVES = 8;
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int CPR = D / 8;                  // 16-byte data chunks per K row
-  static constexpr int KROW = CPR + 1;               // chunks per padded K row
-  static constexpr int VROW = BLK / 8 + 1;           // chunks per padded V^T row (one d, 128 keys)
-  static constexpr int KCH = BLK * KROW;             // chunks of the K tile
-  static constexpr int VCH = D * VROW;               // chunks of the V^T tile
-  static constexpr int BUF_CH = KCH + VCH;           // chunks per buffer
-  static constexpr int SEGS = (BUF_CH + 63) / 64;    // 1-KB load segments per buffer
-  static constexpr int SEG_PER_WAVE = (SEGS + WAVES - 1) / WAVES;
+  // LDS tiles are built from 1-KB segments, one 16-byte global->LDS wavefront
+  // copy each, placed 1040 bytes apart.  A tile of R rows x W bytes has
+  // NI = R W / 1024 segments; row r lives in segment r % NI at position
+  // r / NI, so a segment holds rows s, s+NI, s+2NI, ...  Rows whose indices
+  // differ by less than 16 then start 16 bytes apart modulo 256: the rows
+  // one 16-byte operand fetch reads together hit distinct banks.  A
+  // segment's global source is 1024/W pieces of W contiguous bytes, and a
+  // lane's source offset is a per-lane constant plus s W.
+  static constexpr int SEGB = 1040;
+  static constexpr int KW = D * 2, KNI = BLK * KW / 1024;   // K: 128 rows (keys) x D
+  static constexpr int VW = BLK * 2, VNI = D * VW / 1024;   // V^T: D rows x 128 keys
+  static constexpr int KBYTES = KNI * SEGB, VBYTES = VNI * SEGB;
   static constexpr int KT = BLK / 32, DK = D / 16, DT = D / 32, PS = BLK / 16;
+  static constexpr int KPW = KNI / 4, VPW = VNI / 4;       // copies per wave of a group
+  static_assert(KNI % 4 == 0 && VNI % 4 == 0, "segments split evenly over a wave group");
+  // byte offset of (row, 16-byte chunk) in a tile of NI segments of W-byte rows
+  template <int NI, int W>
+  __host__ __device__ static constexpr int at(int row, int chunk) {
+    return (row % NI) * SEGB + (row / NI) * W + chunk * 16;
+  }
 };
 
-struct RowCursor {
-  int t, r1, kb, kend;
-  bool valid;
+// One mask row's skip list held in registers: lane l holds interval t0 + l
+// (clamped to [0, nKB); lanes past the row's end hold an empty interval).
+// Rows with more than 64 intervals are walked one 64-interval window at a
+// time.  Intervals of a row are ascending and disjoint, as the encoder emits
+// them.
+struct IvWindow {
+  int t0, r1;   // first interval of the window, end of the row's intervals
+  int s, e;     // this lane's interval
 };
 
-__device__ __forceinline__ void cursor_start(RowCursor& c, const int32_t* __restrict__ row_ptr,
-                                             const int32_t* __restrict__ iv, int row, bool exists,
-                                             int nKB) {
-  c.kb = 0;
-  c.kend = 0;
-  c.valid = false;
-  if (!exists) return;
-  c.t = row_ptr[row] - 1;
-  c.r1 = row_ptr[row + 1];
-  c.valid = next_block(iv, c.r1, nKB, c.t, c.kb, c.kend);
+__device__ __forceinline__ void iv_window_load(IvWindow& w, const int32_t* __restrict__ iv, int t0,
+                                               int nKB) {
+  w.t0 = t0;
+  const int t = t0 + (threadIdx.x & 63);
+  w.s = 0;
+  w.e = 0;
+  if (t < w.r1) {
+    w.s = max(iv[2 * t], 0);
+    w.e = min(iv[2 * t + 1], nKB);
+  }
 }
 
+__device__ __forceinline__ void iv_row_start(IvWindow& w, const int32_t* __restrict__ row_ptr,
+                                             const int32_t* __restrict__ iv, int row, bool exists,
+                                             int nKB) {
+  w.r1 = exists ? row_ptr[row + 1] : 0;
+  iv_window_load(w, iv, exists ? row_ptr[row] : 0, nKB);
+}
+
+// Smallest kept block >= x of the row, or INT_MAX.  x only grows between
+// calls, so windows are consumed in order.
+__device__ __forceinline__ int iv_next(IvWindow& w, const int32_t* __restrict__ iv, int x, int nKB) {
+  for (;;) {
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(w.e > x && w.s < w.e);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      return max(__builtin_amdgcn_readlane(w.s, l), x);
+    }
+    if (w.t0 + 64 >= w.r1) return INT_MAX;
+    iv_window_load(w, iv, w.t0 + 64, nKB);
+  }
+}
+
+// S^T (128 keys x 32 queries) = K Q^T.  The scheduling barriers keep the K
+// operands of contraction step kk+1 in flight while step kk computes.
 template <int D>
 __device__ __forceinline__ void mfma_qk(const char* kb_lds, int k_lane, const bf16x8* qreg,
                                         f32x16* sacc) {
   using C = Cfg2<D>;
-  // K operands of contraction step kk+1 are fetched while step kk computes
   uint4 cur[C::KT], nxt[C::KT];
 #pragma unroll
   for (int kt = 0; kt < C::KT; ++kt) {
     sacc[kt] = f32x16{};
-    cur[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + (kt * 32 * C::KROW) * 16);
+    cur[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + kt * 256);   // rows +32
   }
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
     if (kk + 1 < C::DK) {
 #pragma unroll
       for (int kt = 0; kt < C::KT; ++kt)
-        nxt[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + (kt * 32 * C::KROW + 2 * (kk + 1)) * 16);
+        nxt[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + kt * 256 + (kk + 1) * 32);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt)
       sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur[kt]), qreg[kk], sacc[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt) cur[kt] = nxt[kt];
   }
 }
 
+// O^T (D x 32 queries) += V^T P^T, the V^T operands of key step s+1 in flight
+// while step s computes.
 template <int D>
 __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf16x8* pb,
                                         f32x16* oacc) {
   using C = Cfg2<D>;
-  // V^T operands of key step s+1 are fetched while step s computes
+  constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
   uint4 cur[C::DT], nxt[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
-    cur[dt] = *reinterpret_cast<const uint4*>(vb_lds + v_lane + (dt * 32 * C::VROW) * 16);
+    cur[dt] = *reinterpret_cast<const uint4*>(vb_lds + v_lane + dt * DT_OFF);
 #pragma unroll
   for (int s = 0; s < C::PS; ++s) {
     if (s + 1 < C::PS) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
-        nxt[dt] = *reinterpret_cast<const uint4*>(vb_lds + v_lane + (dt * 32 * C::VROW + 2 * (s + 1)) * 16);
+        nxt[dt] = *reinterpret_cast<const uint4*>(vb_lds + v_lane + dt * DT_OFF + (s + 1) * 32);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
       oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur[dt]), pb[s], oacc[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) cur[dt] = nxt[dt];
   }
@@ -413,9 +506,13 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pairs, int pairs_per_xcd) {
   using C = Cfg2<D>;
-  constexpr int KBYTES = C::KCH * 16, VBYTES = C::VCH * 16;
-  __shared__ uint4 lds[(2 * C::KCH + 2 * C::VCH)];   // K buffers 0,1 then V buffers 0,1
-  char* lds_b = reinterpret_cast<char*>(lds);
+  // Separate arrays per buffer, addressed with compile-time buffer indices:
+  // the compiler can then tell that copies in flight target a buffer other
+  // than the one being read, and adds no wait for them before LDS reads.
+  __shared__ uint4 kbuf0[C::KBYTES / 16], kbuf1[C::KBYTES / 16];
+  __shared__ uint4 vbuf0[C::VBYTES / 16], vbuf1[C::VBYTES / 16];
+  char* const kb_lds[2] = {reinterpret_cast<char*>(kbuf0), reinterpret_cast<char*>(kbuf1)};
+  char* const vb_lds[2] = {reinterpret_cast<char*>(vbuf0), reinterpret_cast<char*>(vbuf1)};
 
   // XCD-aware order: workgroup i runs on XCD i % 8; XCD x takes, head after
   // head, the x-th contiguous eighth of that head's query-block pairs.
@@ -428,6 +525,7 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int grp = wave >> 2;
+  const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);   // wave within its group
   const int n = lane & 31, h = lane >> 5;
   const int N = a.N;
   const int qb0 = 2 * pair;
@@ -439,9 +537,9 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   const int64_t head_off = int64_t(bh) * N * D;
   const __bf16* Q = static_cast<const __bf16*>(tm ? a.qp : a.q) + head_off;
   const char* Kh = reinterpret_cast<const char*>(static_cast<const __bf16*>(tm ? a.kp : a.k) + head_off);
-    __bf16* O = static_cast<__bf16*>(tm ? a.op : a.o) + head_off;
+  __bf16* O = static_cast<__bf16*>(tm ? a.op : a.o) + head_off;
 
-  const int q_row = (qb0 + grp) * C::BLK + (wave & 3) * 32 + n;
+  const int q_row = (qb0 + grp) * C::BLK + w4 * 32 + n;
   bf16x8 qreg[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
@@ -450,53 +548,37 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
     qreg[kk] = as_bf16x8(u);
   }
 
-  // This thread's share of the 16-byte global->LDS copies of one key block:
-  // K chunks first, then V chunks, 1 KB per wavefront instruction; lanes on
-  // row padding stay idle.  Source offset inside the block (bytes) or -1.
-  constexpr int KSEG = (C::KCH + 63) / 64, VSEG = (C::VCH + 63) / 64;
-  constexpr int KPW = (KSEG + C::WAVES - 1) / C::WAVES, VPW = (VSEG + C::WAVES - 1) / C::WAVES;
-  int ksrc[KPW], vsrc[VPW];
-#pragma unroll
-  for (int u = 0; u < KPW; ++u) {
-    const int p = (u * C::WAVES + wave) * 64 + lane;
-    const int r = p / C::KROW, c = p % C::KROW;
-    ksrc[u] = (p < C::KCH && c < C::CPR) ? (r * D + c * 8) * 2 : -1;
-  }
-#pragma unroll
-  for (int u = 0; u < VPW; ++u) {
-    const int p = (u * C::WAVES + wave) * 64 + lane;
-    const int r = p / C::VROW, c = p % C::VROW;
-    vsrc[u] = (p < C::VCH && c < C::BLK / 8) ? (r * C::BLK + c * 8) * 2 : -1;
-  }
-  // Keys past N (ragged last block) read row N-1 instead: finite values whose
-  // scores are masked to -inf and whose P weights are 0.
-  auto load_k = [&](int kb, char* dst) {
-    const char* blk = Kh + int64_t(kb) * C::BLK * D * 2;
-    const int last = N - 1 - kb * C::BLK;   // last valid row of this block
-#pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      const int seg = u * C::WAVES + wave;
-      int off = ksrc[u];
-      if (seg < KSEG && off >= 0) {
-        const int r = off / (D * 2);
-        if (r > last) off += (last - r) * D * 2;
-        __builtin_amdgcn_global_load_lds((GLB_AS void*)(blk + off), (LDS_AS void*)(dst + seg * 1024),
-                                         16, 0, 0);
-      }
-    }
+  // Copies of a group: wave w4 takes the tile's segments w4*PW .. w4*PW+PW-1.
+  // Per lane, the global source offset is lane_src + s * W for segment s.
+  const uint32_t k_lane_src = (lane / (C::KW / 16)) * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
+  const uint32_t v_lane_src = (lane / (C::VW / 16)) * C::VNI * C::VW + (lane % (C::VW / 16)) * 16;
+  const uint32_t k_w4_src = w4 * C::KPW * C::KW, v_w4_src = w4 * C::VPW * C::VW;
+  // K rows past N (ragged last block) fall outside the block's buffer range
+  // and are never fetched: their scores are masked to -inf.  A block that
+  // does not exist gets an empty range: its copies fetch nothing.
+  auto k_src = [&](int kb, bool exists) {
+    return LdsCopySrc(Kh + int64_t(exists ? kb : 0) * C::BLK * D * 2,
+                      exists ? min(C::BLK, N - kb * C::BLK) * D * 2 : 0);
   };
   // V^T tiles come from the block-transposed workspace: [D][128] per block,
   // keys past N already zero
   const char* Vt = static_cast<const char*>(a.vt) + int64_t(bh) * a.n_kb * C::BLK * D * 2;
-  auto load_v = [&](int kb, char* dst) {
-    const char* blk = Vt + int64_t(kb) * C::BLK * D * 2;
-#pragma unroll
-    for (int u = 0; u < VPW; ++u) {
-      const int seg = u * C::WAVES + wave;
-      if (seg < VSEG && vsrc[u] >= 0)
-        __builtin_amdgcn_global_load_lds((GLB_AS void*)(blk + vsrc[u]),
-                                         (LDS_AS void*)(dst + seg * 1024), 16, 0, 0);
-    }
+  auto v_src = [&](int kb, bool exists) {
+    return LdsCopySrc(Vt + int64_t(exists ? kb : 0) * C::BLK * D * 2, exists ? C::BLK * D * 2 : 0);
+  };
+  auto copy_k = [&](const LdsCopySrc& src, const char* dst) {
+    const uint32_t lds_w = lds_addr_of(dst) + w4 * C::KPW * C::SEGB;
+    static_for<C::KPW>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      src.copy16(k_lane_src, sadd<u * C::KW>(k_w4_src), sadd<u * C::SEGB>(lds_w));
+    });
+  };
+  auto copy_v = [&](const LdsCopySrc& src, const char* dst) {
+    const uint32_t lds_w = lds_addr_of(dst) + w4 * C::VPW * C::SEGB;
+    static_for<C::VPW>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      src.copy16(v_lane_src, sadd<u * C::VW>(v_w4_src), sadd<u * C::SEGB>(lds_w));
+    });
   };
 
   f32x16 oacc[C::DT];
@@ -507,60 +589,64 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   f32x16 sacc[C::KT];
   bf16x8 pb[C::PS];
 
-  RowCursor ca, cb;
-  cursor_start(ca, a.row_ptr, a.iv, mask_id * a.n_qb + qb0, true, a.n_kb);
-  cursor_start(cb, a.row_ptr, a.iv, mask_id * a.n_qb + qb0 + 1, has_b, a.n_kb);
+  IvWindow wa, wb;
+  iv_row_start(wa, a.row_ptr, a.iv, mask_id * a.n_qb + qb0, true, a.n_kb);
+  iv_row_start(wb, a.row_ptr, a.iv, mask_id * a.n_qb + qb0 + 1, has_b, a.n_kb);
+  int na = iv_next(wa, a.iv, 0, a.n_kb), nb = iv_next(wb, a.iv, 0, a.n_kb);
   // merged block sequence of the two rows; `mine` = the block is in my row
   auto pick = [&](int& kb, bool& mine) -> bool {
-    if (!ca.valid && !cb.valid) return false;
-    kb = min(ca.valid ? ca.kb : INT_MAX, cb.valid ? cb.kb : INT_MAX);
-    const bool in_a = ca.valid && ca.kb == kb;
-    const bool in_b = cb.valid && cb.kb == kb;
-    if (in_a) ca.valid = next_block(a.iv, ca.r1, a.n_kb, ca.t, ca.kb, ca.kend);
-    if (in_b) cb.valid = next_block(a.iv, cb.r1, a.n_kb, cb.t, cb.kb, cb.kend);
+    kb = min(na, nb);
+    if (kb == INT_MAX) return false;
+    const bool in_a = na == kb, in_b = nb == kb;
+    if (in_a) na = iv_next(wa, a.iv, kb + 1, a.n_kb);
+    if (in_b) nb = iv_next(wb, a.iv, kb + 1, a.n_kb);
     mine = grp == 0 ? in_a : in_b;
     return true;
   };
 
   const int srow = swap_bits23(n);
   const float c2 = a.scale_log2;
-  const int k_lane = (srow * C::KROW + h) * 16;
-  const int v_lane = (n * C::VROW + h) * 16;   // V^T row d = n (+32*dt), keys 8h.. (+16s)
+  const int k_lane = C::template at<C::KNI, C::KW>(srow, h);   // K row srow (+32 kt), chunk h (+2 kk)
+  const int v_lane = C::template at<C::VNI, C::VW>(n, h);      // V^T row n (+32 dt), chunk h (+2 s)
 
   // cur: block j (K_j staged / being used); prev: block j-1 (V_{j-1})
   int kb_cur = 0, kb_prev = 0;
   bool mine_cur = false, mine_prev = false;
   bool have_cur = pick(kb_cur, mine_cur);
   bool have_prev = false;
-  if (have_cur) load_k(kb_cur, lds_b);
+  if (grp == 0) copy_k(k_src(kb_cur, have_cur), kb_lds[0]);
   __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
-  __syncthreads();
+  barrier_lds();
 
-  int j = 0;
-  while (have_cur || have_prev) {
-    const int kbuf = j & 1;
-    char* k_cur = lds_b + kbuf * KBYTES;
-    char* v_prev = lds_b + 2 * KBYTES + (kbuf ^ 1) * VBYTES;
-    // loads for the next iteration: K_{j+1}, V_j
+  // Iteration j uses K buffer j%2 and V buffer (j-1)%2; unrolled by two so
+  // that every buffer is a compile-time object.
+  auto iteration = [&](auto kbuf_c) {
+    constexpr int kbuf = decltype(kbuf_c)::value;
+    const char* k_cur = kb_lds[kbuf];
+    const char* v_prev = vb_lds[kbuf ^ 1];
     int kb_next = 0;
     bool mine_next = false;
     const bool have_next = have_cur && pick(kb_next, mine_next);
-    if (have_next) load_k(kb_next, lds_b + (kbuf ^ 1) * KBYTES);
-    if (have_cur) load_v(kb_cur, lds_b + 2 * KBYTES + kbuf * VBYTES);
 
     // ---- phase 1 --------------------------------------------------------------
     if (grp == 0) {
       if (have_prev && mine_prev) mfma_pv<D>(v_prev, v_lane, pb, oacc);
       if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
     } else {
+      // V^T of block j into the V buffer freed by block j-2
+      copy_v(v_src(kb_cur, have_cur), vb_lds[kbuf]);
+      __builtin_amdgcn_sched_barrier(0);
       if (have_prev && mine_prev)
         softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_prev * C::BLK, N, h, c2);
     }
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase 2 --------------------------------------------------------------
     if (grp == 0) {
+      // K of block j+1 into the K buffer freed by block j-1
+      copy_k(k_src(kb_next, have_next), kb_lds[kbuf ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
       if (have_cur && mine_cur)
         softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_cur * C::BLK, N, h, c2);
     } else {
@@ -568,8 +654,8 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
       if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
     }
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this thread's loads have landed
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
+    barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
 
     kb_prev = kb_cur;
@@ -578,7 +664,11 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
     kb_cur = kb_next;
     mine_cur = mine_next;
     have_cur = have_next;
-    ++j;
+  };
+  while (have_cur || have_prev) {
+    iteration(std::integral_constant<int, 0>{});
+    if (!(have_cur || have_prev)) break;
+    iteration(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -592,7 +682,7 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
       for (int g = 0; g < 4; ++g) {
         bf16x4 w;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) w[jj] = (__bf16)(oacc[dt][4 * g + jj] * inv);
+        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[dt][4 * g + j] * inv);
         *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * h) = w;
       }
     }

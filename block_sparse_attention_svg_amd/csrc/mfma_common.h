@@ -44,6 +44,15 @@ __device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
   }
 }
 
+// Workgroup barrier that waits only for this thread's LDS operations.  Unlike
+// __syncthreads() it does not drain outstanding global loads, so 16-byte
+// global->LDS copies of later tiles stay in flight across it; callers wait
+// for the copies they need with an explicit vmcnt first.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }

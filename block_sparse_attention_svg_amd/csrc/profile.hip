@@ -12,9 +12,13 @@
 //
 // Pass 1 (profile_partial_kernel): split-K over key chunks.  One workgroup per
 //   (chunk, batch*head), four wavefronts of 16 sampled queries each.  Key
-//   tiles of 64 are staged in LDS (K row-major, V transposed); S^T = K Q^T and
-//   U_c^T += V^T P_c^T run on v_mfma_f32_16x16x32_bf16; each class keeps its
-//   own running max.  Writes (m_c, Z_c, U_c) per (chunk, sample, class).
+//   tiles of 64 stream through double-buffered, padded LDS by 16-byte
+//   global->LDS copies; S^T = K Q^T and U_c^T += V^T P_c^T run on
+//   v_mfma_f32_16x16x32_bf16, the V^T operand coming from transposing LDS
+//   reads, Z_c from one more MFMA with an all-ones operand.  Each class keeps
+//   its own running max; within a 32-key step the spatial admission is the
+//   same for all keys of a query, so only two classes are live per lane.
+//   Writes (m_c, Z_c, U_c) per (chunk, sample, class).
 // Pass 2 (profile_merge_kernel): one workgroup per (batch*head, sample):
 //   merges the chunks in a fixed order and evaluates both errors.
 // Pass 3 (profile_choose_kernel): sums the samples in order, picks the head's
@@ -26,6 +30,8 @@
 // lane l holds row 4*(l/16)+r, column l%16.  The two 16-key S^T tiles of a
 // 32-key step fetch K rows in the order 8*(m/4) + 4*tile + m%4, so lane
 // group g = l/16 ends up holding keys 8g..8g+7, exactly its P^T operand.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "svg_internal.h"
 
@@ -33,22 +39,29 @@ namespace svg {
 namespace {
 
 constexpr int kQ = 64;          // samples per workgroup (4 waves x 16)
-constexpr int kTK = 64;         // keys staged per LDS tile
+constexpr int kTK = 32;         // keys staged per LDS tile (one 32-key step)
 constexpr int kThreads = 256;
 constexpr int kMaxWords = 32;   // bitmap words per row held in LDS (nB <= 1024)
 constexpr int kChunkKeys = 4096;
 constexpr float kRescaleLog2 = 8.0f;
 
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
 template <int D>
 struct PCfg {
-  static constexpr int DK = D / 32;   // 16x16x32 steps of the QK^T contraction
-  static constexpr int DT = D / 16;   // 16-row tiles of U^T
-  using KTile = LdsTile<kTK, D>;
-  using VTile = LdsTile<D, kTK>;
-  static constexpr int K_LOADS = KTile::CHUNKS / kThreads;
-  static constexpr int V_TASKS = (kTK / 8) * (D / 8);
-  static constexpr int V_PER_T = (V_TASKS + kThreads - 1) / kThreads;
-  static constexpr int REC = D + 4;   // floats per (sample, class) record: m, Z, pad, U[D]
+  static constexpr int DK = D / 32;      // 16x16x32 steps of the QK^T contraction
+  static constexpr int DT = D / 16;      // 16-row tiles of U^T
+  static constexpr int CPR = D / 8;      // 16-byte chunks per K / V row
+  static constexpr int KROW = CPR + 1;   // padded K row (D+8 elements): conflict-free b128 fetches
+  static constexpr int VROW = CPR + 4;   // padded V row (D+32): conflict-free transposing fetches
+  static constexpr int KCH = kTK * KROW, VCH = kTK * VROW, BUF = KCH + VCH;
+  static constexpr int SEGS = (BUF + 63) / 64;
+  static constexpr int SPW = (SEGS + 3) / 4;   // load instructions per wave per tile
+  static constexpr int STAGES = 3;             // ring of tiles: two loads in flight
+  static constexpr int STRIDE = SEGS * 64;     // chunks per stage (whole 1-KB segments)
+  static constexpr int DUMMY = STAGES * STRIDE;  // 1-KB sink for surplus segments
+  static constexpr int REC = D + 4;      // floats per (sample, class) record: m, Z, pad, U[D]
 };
 
 struct Geo {
@@ -64,14 +77,15 @@ __device__ __forceinline__ int token_major(int j, const Geo& g) {
   return s * g.F + f;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void profile_partial_kernel(ProfileArgs a, Geo g) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void profile_partial_kernel(ProfileArgs a, Geo g) {
   using C = PCfg<D>;
-  __shared__ uint4 Ks[C::KTile::CHUNKS];
-  __shared__ uint4 Vt[C::VTile::CHUNKS];
+  __shared__ uint4 lds[C::STAGES * C::STRIDE + 64];   // ring stages, then a 1-KB sink
   __shared__ uint32_t rowS[kQ][kMaxWords];
   __shared__ uint32_t rowT[kQ][kMaxWords];
-  __shared__ int blkT[kTK];
+  __shared__ int blkT[C::STAGES][kTK];
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -79,23 +93,21 @@ __global__ __launch_bounds__(kThreads) void profile_partial_kernel(ProfileArgs a
   const int N = g.N;
   const int64_t head_off = int64_t(bh) * N * D;
   const __bf16* Qh = static_cast<const __bf16*>(a.q) + head_off;
-  const uint4* Kg = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.k) + head_off);
-  const uint4* Vg = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(a.v) + head_off);
+  const char* Kh = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.k) + head_off);
+  const char* Vh = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.v) + head_off);
 
   // bitmap rows of every sample: spatial row = frame-major block of the query,
   // temporal row = token-major block of the query
   for (int e = tid; e < kQ * a.W; e += kThreads) {
-    int sidx = e / a.W, w = e % a.W;
+    int si = e / a.W, w = e % a.W;
     uint32_t ws = 0, wt = 0;
-    if (sidx < a.n_samples) {
-      int qi = min(max(a.idx[sidx], 0), g.Nv - 1);
-      int rs = qi >> g.blk_log2;
-      int rt = token_major(qi, g) >> g.blk_log2;
-      ws = a.bitmap[int64_t(rs) * a.W + w];
-      wt = a.bitmap[int64_t(a.nB + rt) * a.W + w];
+    if (si < a.n_samples) {
+      int qi = min(max(a.idx[si], 0), g.Nv - 1);
+      ws = a.bitmap[int64_t(qi >> g.blk_log2) * a.W + w];
+      wt = a.bitmap[int64_t(a.nB + (token_major(qi, g) >> g.blk_log2)) * a.W + w];
     }
-    rowS[sidx][w] = ws;
-    rowT[sidx][w] = wt;
+    rowS[si][w] = ws;
+    rowT[si][w] = wt;
   }
 
   // Q operand: lane holds sample wave*16 + n, dims 32*kk + 8*grp + i
@@ -112,140 +124,180 @@ __global__ __launch_bounds__(kThreads) void profile_partial_kernel(ProfileArgs a
     }
   }
 
-  f32x4 uacc[4][C::DT];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) uacc[c][dt] = f32x4{};
-  float mrun[4], zpart[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) { mrun[c] = -INFINITY; zpart[c] = 0.f; }
-
   const int k_begin = chunk * a.chunk_keys;
   const int k_end = min(N, k_begin + a.chunk_keys);
-  constexpr int CPR = D / 8;
+  const int n_tiles = (k_end - k_begin + kTK - 1) / kTK;
 
-  uint4 kst[C::K_LOADS];
-  uint4 vst[C::V_PER_T][8];
-  auto load = [&](int key0) {
+  // this thread's 16-byte global->LDS copies of one tile (K chunks, then V
+  // chunks; lanes on row padding idle): byte offset inside the tile's rows,
+  // bit 30 marking V, -1 when idle
+  int src[C::SPW];
 #pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u) {
-      int c = tid + u * kThreads;
-      int key = key0 + c / CPR;
-      kst[u] = key < k_end ? Kg[int64_t(key) * CPR + c % CPR] : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < C::SPW; ++u) {
+    const int p = (u * 4 + wave) * 64 + lane;
+    int off = -1;
+    if (p < C::KCH) {
+      const int r = p / C::KROW, c = p % C::KROW;
+      if (c < C::CPR) off = (r * D + c * 8) * 2;
+    } else if (p < C::BUF) {
+      const int r = (p - C::KCH) / C::VROW, c = (p - C::KCH) % C::VROW;
+      if (c < C::CPR) off = ((r * D + c * 8) * 2) | (1 << 30);
     }
+    src[u] = off;
+  }
+  // Every wave issues exactly SPW copies per tile, so vmcnt(SPW) waits for
+  // precisely the oldest tile in flight.  The LDS destination of a copy is
+  // wave-uniform: lanes on row padding fill padding of their own stage, and
+  // segments past the tile go to a sink.
+  char* lds_b = reinterpret_cast<char*>(lds);
+  auto stage = [&](int key0, int b) {
+    char* sbase = lds_b + b * C::STRIDE * 16;
+    const int last = k_end - 1 - key0;   // rows past the chunk read its last row (masked later)
 #pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      int t = tid + u * kThreads;
-      int kg = t % (kTK / 8), dc = t / (kTK / 8);
-      if (t < C::V_TASKS) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          int key = key0 + 8 * kg + i;
-          vst[u][i] = key < k_end ? Vg[int64_t(key) * CPR + dc] : make_uint4(0, 0, 0, 0);
-        }
+    for (int u = 0; u < C::SPW; ++u) {
+      const int seg = u * 4 + wave;
+      int off = 0;
+      const char* base = Kh;
+      if (src[u] >= 0) {
+        off = src[u] & ~(1 << 30);
+        base = (src[u] & (1 << 30)) ? Vh : Kh;
+        const int r = off / (D * 2);
+        if (r > last) off += (last - r) * D * 2;
       }
+      char* dst = seg < C::SEGS ? sbase + seg * 64 * 16 : lds_b + C::DUMMY * 16;
+      __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + int64_t(key0) * D * 2 + off),
+                                       (LDS_AS void*)dst, 16, 0, 0);
+    }
+    if (tid < kTK) {
+      const int key = min(key0 + tid, k_end - 1);
+      blkT[b][tid] = token_major(key, g) >> g.blk_log2;
     }
   };
 
-  if (k_begin < k_end) load(k_begin);
-  for (int key0 = k_begin; key0 < k_end; key0 += kTK) {
-    __syncthreads();
+  f32x4 uacc[4][C::DT];
+  f32x4 zacc[4];
 #pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u) {
-      int c = tid + u * kThreads;
-      Ks[C::KTile::slot(c / CPR, c % CPR)] = kst[u];
-    }
+  for (int c = 0; c < 4; ++c) {
+    zacc[c] = f32x4{};
 #pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      int t = tid + u * kThreads;
-      if (t < C::V_TASKS) {
-        int kg = t % (kTK / 8), dc = t / (kTK / 8);
-        uint4 cols[8];
-        transpose8x8(vst[u], cols);
+    for (int dt = 0; dt < C::DT; ++dt) uacc[c][dt] = f32x4{};
+  }
+  float mrun[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Vt[C::VTile::slot(8 * dc + j, kg)] = cols[j];
-      }
-    }
-    if (tid < kTK) {
-      int key = key0 + tid;
-      blkT[tid] = key < k_end ? (token_major(key, g) >> g.blk_log2) : 0;
-    }
-    __syncthreads();
-    if (key0 + kTK < k_end) load(key0 + kTK);
+  for (int c = 0; c < 4; ++c) mrun[c] = -INFINITY;
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
 
+  const int k_lane = ((8 * (n >> 2) + (n & 3)) * C::KROW + grp) * 16;   // tile 0, kk 0
+  const int v_lane = C::KCH * 16 + ((8 * grp + (n >> 2)) * C::VROW) * 16 + ((n & 3) * 4) * 2;
+  const float c2 = a.scale_log2;
+
+  if (n_tiles > 0) stage(k_begin, 0);
+  if (n_tiles > 1) stage(k_begin + kTK, 1);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int b = t % C::STAGES;
+    const int key0 = k_begin + t * kTK;
+    // this thread's copies of tile t have landed (tile t+1 may still fly)
+    if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x3f70 | C::SPW);   // vmcnt(SPW)
+    else __builtin_amdgcn_s_waitcnt(0x3f70);                            // vmcnt(0)
+    barrier_lds();     // everyone's copies landed; stage (t+2)%3 is no longer read
+    if (t + 2 < n_tiles) stage(key0 + 2 * kTK, (t + 2) % C::STAGES);
+    const char* lb = lds_b + b * C::STRIDE * 16;
 #pragma unroll
     for (int half = 0; half < kTK / 32; ++half) {
-      // ---- S^T for 32 keys: two 16x16 tiles ---------------------------------
+      // ---- S^T for 32 keys: two 16x16 tiles; lane (n, grp) gets keys 8*grp + i
       f32x4 s2[2];
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
         s2[tile] = f32x4{};
-        const int krow = half * 32 + 8 * (n >> 2) + 4 * tile + (n & 3);
 #pragma unroll
         for (int kk = 0; kk < C::DK; ++kk) {
-          bf16x8 kop = as_bf16x8(Ks[C::KTile::slot(krow, 4 * kk + grp)]);
-          s2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], s2[tile], 0, 0, 0);
+          const uint4 raw = *reinterpret_cast<const uint4*>(
+              lb + k_lane + ((half * 32 + 4 * tile) * C::KROW + 4 * kk) * 16);
+          s2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(raw), qreg[kk], s2[tile], 0, 0, 0);
         }
       }
-      // lane (n, grp) now holds keys half*32 + 8*grp + i, i = 0..7
       const int kbase = key0 + half * 32;
-      const int kblock = min(kbase >> g.blk_log2, a.nB - 1);  // one key block for all 32 keys
+      const int kblock = min(kbase >> g.blk_log2, a.nB - 1);   // one key block for all 32 keys
       const bool inS = svalid && ((rowS[sidx][kblock >> 5] >> (kblock & 31)) & 1u);
       float x[8];
-      int cls[8];
+      bool inT[8];
+      float m_in = -INFINITY, m_out = -INFINITY;   // this lane's max over T-kept / T-skipped keys
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int kl = half * 32 + 8 * grp + i;
-        const int key = key0 + kl;
-        const int bt = blkT[kl];
-        const bool inT = (rowT[sidx][bt >> 5] >> (bt & 31)) & 1u;
-        cls[i] = (inS ? 0 : 2) + (inT ? 0 : 1);
-        const float sv = s2[i >> 2][i & 3] * a.scale_log2;
-        x[i] = (key < k_end && svalid) ? sv : -INFINITY;
+        const int bt = blkT[b][kl];
+        inT[i] = (rowT[sidx][bt >> 5] >> (bt & 31)) & 1u;
+        const bool ok = svalid && key0 + kl < k_end;
+        x[i] = ok ? s2[i >> 2][i & 3] : -INFINITY;
+        m_in = fmaxf(m_in, inT[i] ? x[i] : -INFINITY);
+        m_out = fmaxf(m_out, inT[i] ? -INFINITY : x[i]);
       }
-      // per-class block max, combined over the 4 lane groups of a sample
-      float mx[4];
+      m_in *= c2;
+      m_out *= c2;
+      // the two classes live in this step: (both, S only) if inS, else (T only, none)
+      float r_in = inS ? mrun[0] : mrun[2];
+      float r_out = inS ? mrun[1] : mrun[3];
+      // Fast path: no lane's block max exceeds its running max by more than
+      // 2^8, so the stale maxima stay valid and no cross-lane exchange is
+      // needed.  Otherwise combine the maxima over the 4 lanes of each sample
+      // and rescale the classes whose maximum moved.
+      if (__ballot(m_in > r_in + kRescaleLog2 || m_out > r_out + kRescaleLog2)) {
+        m_in = fmaxf(m_in, shfl_xor_f(m_in, 16));
+        m_in = fmaxf(m_in, shfl_xor_f(m_in, 32));
+        m_out = fmaxf(m_out, shfl_xor_f(m_out, 16));
+        m_out = fmaxf(m_out, shfl_xor_f(m_out, 32));
+        const bool up_in = m_in > r_in + kRescaleLog2;
+        const bool up_out = m_out > r_out + kRescaleLog2;
+        const float al_in = up_in ? fast_exp2(r_in - m_in) : 1.f;
+        const float al_out = up_out ? fast_exp2(r_out - m_out) : 1.f;
+        float f[4];
+        f[0] = inS ? al_in : 1.f;
+        f[1] = inS ? al_out : 1.f;
+        f[2] = inS ? 1.f : al_in;
+        f[3] = inS ? 1.f : al_out;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float m = -INFINITY;
+        for (int c = 0; c < 4; ++c) {
+          zacc[c] *= f[c];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, cls[i] == c ? x[i] : -INFINITY);
-        m = fmaxf(m, shfl_xor_f(m, 16));
-        m = fmaxf(m, shfl_xor_f(m, 32));
-        mx[c] = m;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (mx[c] > mrun[c] + kRescaleLog2) {
-          const float alpha = fast_exp2(mrun[c] - mx[c]);
-          zpart[c] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt) uacc[c][dt] *= alpha;
-          mrun[c] = mx[c];
+          for (int dt = 0; dt < C::DT; ++dt) uacc[c][dt] *= f[c];
         }
+        if (up_in) r_in = m_in;
+        if (up_out) r_out = m_out;
+        mrun[0] = inS ? r_in : mrun[0];
+        mrun[1] = inS ? r_out : mrun[1];
+        mrun[2] = inS ? mrun[2] : r_in;
+        mrun[3] = inS ? mrun[3] : r_out;
       }
-      bf16x8 pb[4];
+      bf16x8 pin, pout;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int c = cls[i];
-        const float mref = c == 0 ? mrun[0] : c == 1 ? mrun[1] : c == 2 ? mrun[2] : mrun[3];
-        const float p = x[i] == -INFINITY ? 0.f : fast_exp2(x[i] - mref);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const float pc = c == cc ? p : 0.f;
-          zpart[cc] += pc;
-          pb[cc][i] = (__bf16)pc;
-        }
+        const float p = fast_exp2(__builtin_fmaf(x[i], c2, -(inT[i] ? r_in : r_out)));
+        const __bf16 pb = (__bf16)p;
+        pin[i] = inT[i] ? pb : (__bf16)0.0f;
+        pout[i] = inT[i] ? (__bf16)0.0f : pb;
       }
-      // ---- U_c^T += V^T P_c^T -------------------------------------------------
+      const bf16x8 zero8 = {};
+      bf16x8 pc[4];
+      pc[0] = inS ? pin : zero8;
+      pc[1] = inS ? pout : zero8;
+      pc[2] = inS ? zero8 : pin;
+      pc[3] = inS ? zero8 : pout;
+      // ---- U_c^T += V^T P_c^T; Z_c from an all-ones operand ------------------
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        bf16x8 vop = as_bf16x8(Vt[C::VTile::slot(dt * 16 + n, 4 * half + grp)]);
+        const char* p0 = lb + v_lane + (half * 32 * C::VROW) * 16 + dt * 32;
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 4 * C::VROW * 16));
+        const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          uacc[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[c], uacc[c][dt], 0, 0, 0);
+          uacc[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pc[c], uacc[c][dt], 0, 0, 0);
       }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[c], zacc[c], 0, 0, 0);
     }
   }
 
@@ -253,13 +305,10 @@ __global__ __launch_bounds__(kThreads) void profile_partial_kernel(ProfileArgs a
   float* rec = a.ws + ((int64_t(bh) * a.n_chunks + chunk) * kQ + sidx) * 4 * C::REC;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    float z = zpart[c];
-    z += shfl_xor_f(z, 16);
-    z += shfl_xor_f(z, 32);
     float* r = rec + c * C::REC;
     if (grp == 0) {
       r[0] = mrun[c];
-      r[1] = z;
+      r[1] = zacc[c][0];
     }
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -375,7 +424,11 @@ size_t profile_workspace_bytes(int BH, int N, int D, int block, int n_samples, i
                                int* n_chunks) {
   (void)block;
   (void)n_samples;
-  int ck = kChunkKeys;
+  // about 1024 workgroups (two full rounds of two per CU), chunks of at least
+  // one 32-key tile and at most kChunkKeys keys
+  const int target = ceil_div(1024, BH);
+  int ck = ceil_div(ceil_div(N, target), kTK) * kTK;
+  ck = min(max(ck, kTK), kChunkKeys);
   int nc = ceil_div(N, ck);
   if (chunk_keys) *chunk_keys = ck;
   if (n_chunks) *n_chunks = nc;
