@@ -487,20 +487,21 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
     for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
     m_run = mx;
   }
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // The denominator sums the fp32 weights with plain adds (two chains): a
+  // bf16 dot2 would have to wait for the matrix core, which the partner wave
+  // on this SIMD keeps busy during the softmax.
+  float l0 = 0.f, l1 = 0.f;
 #pragma unroll
   for (int s = 0; s < C::PS; ++s) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pb[s][i] = (__bf16)fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + i], c2, -m_run));
-    // denominator from the same bf16 weights the PV product uses
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const bf16x2 pair = {pb[s][i], pb[s][i + 1]};
-      l_part = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_part, false);
+    for (int i = 0; i < 8; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + i], c2, -m_run));
+      pb[s][i] = (__bf16)p;
+      if (i & 1) l1 += p;
+      else l0 += p;
     }
   }
+  l_part += l0 + l1;
 }
 
 template <int D>

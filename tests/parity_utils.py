@@ -7,9 +7,10 @@ import torch
 # attention outputs: bf16 inputs, fp32 accumulation, bf16 output
 ATTN_MAX_ABS = 2e-2
 ATTN_REL_L2 = 5e-3
-# log-sum-exp: the denominator sums the bf16-rounded weights that the PV product
-# uses; each carries at most 2^-9 relative rounding, so |d lse| <= ln(1 + 2^-9)
-# = 1.95e-3, plus fp32 accumulation error
+# log-sum-exp: the kernels sum the fp32 weights (the PV product uses them rounded
+# to bf16).  The bound is the one for a denominator of bf16-rounded weights,
+# each within 2^-9 relative: |d lse| <= ln(1 + 2^-9) = 1.95e-3, plus fp32
+# accumulation error; a denominator of fp32 weights stays well inside it.
 LSE_ABS = 2.5e-3
 
 
