@@ -42,7 +42,7 @@ constexpr int kQ = 64;          // samples per workgroup (4 waves x 16)
 constexpr int kTK = 32;         // keys staged per LDS tile (one 32-key step)
 constexpr int kThreads = 256;
 constexpr int kMaxWords = 32;   // bitmap words per row held in LDS (nB <= 1024)
-constexpr int kChunkKeys = 4096;
+constexpr int kChunkKeys = 32768;
 constexpr float kRescaleLog2 = 8.0f;
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -424,12 +424,25 @@ size_t profile_workspace_bytes(int BH, int N, int D, int block, int n_samples, i
                                int* n_chunks) {
   (void)block;
   (void)n_samples;
-  // about 1024 workgroups (two full rounds of two per CU), chunks of at least
-  // one 32-key tile and at most kChunkKeys keys
-  const int target = ceil_div(1024, BH);
-  int ck = ceil_div(ceil_div(N, target), kTK) * kTK;
-  ck = min(max(ck, kTK), kChunkKeys);
-  int nc = ceil_div(N, ck);
+  // Chunking: the partial kernel runs two workgroups per CU, 512 at a time on
+  // the 256 CUs of an MI355X.  The chunk length (whole 32-key tiles, at most
+  // kChunkKeys keys) minimises a cost in units of one tile's time: rounds of
+  // workgroups x (tiles per workgroup + about 3 tiles of set-up), plus the
+  // chunk records written and merged (about 0.031 tile per record set of a
+  // head, 64 samples x 4 classes x (D + 4) floats, at HBM speed).
+  constexpr int kSlots = 512;
+  int ck = kTK, nc = ceil_div(N, kTK);
+  long best = -1;
+  for (int t = kTK; t <= kChunkKeys; t += kTK) {
+    const int c = ceil_div(N, t);
+    const long cost = long(ceil_div(BH * c, kSlots)) * (t / kTK + 3) * 1000 + 31L * BH * c;
+    if (best < 0 || cost < best) {
+      best = cost;
+      ck = t;
+      nc = c;
+    }
+    if (c == 1) break;
+  }
   if (chunk_keys) *chunk_keys = ck;
   if (n_chunks) *n_chunks = nc;
   size_t rec = records_bytes(BH, D, nc);
