@@ -273,7 +273,8 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_fwd_kernel(AttnArgs a) {
 // Each key block j passes through two phases.  Phase 1: group 0 runs the
 // MFMAs (O += P_{j-1} V_{j-1}, S_j = Q K_j^T) while group 1 runs the softmax
 // of S_{j-1}; phase 2 swaps the roles.  The two waves sharing a SIMD thus
-// alternate between matrix work and VALU work.  K_j and V^T_j land in
+// alternate between matrix work and VALU work; one barrier per block (at its
+// end) orders the buffer refills.  K_j and V^T_j land in
 // double-buffered LDS through 16-byte global->LDS copies issued by the group
 // doing softmax: V^T of block j in phase 1 (group 1), K of block j+1 in
 // phase 2 (group 0).  The copies go out before that group's softmax and land
@@ -640,8 +641,10 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
       if (have_prev && mine_prev)
         softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_prev * C::BLK, N, h, c2);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    barrier_lds();
+    // No barrier between the phases: the groups share no data within an
+    // iteration (each holds its own S, P and O; the copies of this iteration
+    // refill buffers last read in the previous one), so a group that is done
+    // early starts its next phase at once.
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase 2 --------------------------------------------------------------
     if (grp == 0) {
