@@ -227,6 +227,11 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
   a.N = s.N; a.D = s.D; a.block = s.block;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.vt = workspace;
+  a.plan = nullptr;
+  a.bitmap = masks->bitmap;
+  if (need > 0)
+    a.plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                        (need - attn_plan_bytes(a.BH, (a.n_qb + 1) / 2)));
   launch_attn(a, as_stream(stream));
   return check_launch(fn);
 }

@@ -516,13 +516,18 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   char* const kb_lds[2] = {reinterpret_cast<char*>(kbuf0), reinterpret_cast<char*>(kbuf1)};
   char* const vb_lds[2] = {reinterpret_cast<char*>(vbuf0), reinterpret_cast<char*>(vbuf1)};
 
-  // XCD-aware order: workgroup i runs on XCD i % 8; XCD x takes, head after
-  // head, the x-th contiguous eighth of that head's query-block pairs.
+  // XCD-aware order: workgroup i runs on XCD i % 8 and takes item i / 8 of
+  // that XCD's work list (plan_kernel, order_kernel): the x-th of eight
+  // contiguous ranges of every head's query-block pairs, ranges of about equal
+  // work, heavy pairs first, otherwise head after head and pair after pair,
+  // so consecutive workgroups read the same key blocks through one L2.
   const int xcd = blockIdx.x % 8;
   const int local = blockIdx.x / 8;
-  const int bh = local / pairs_per_xcd;
-  const int pair = xcd * pairs_per_xcd + local % pairs_per_xcd;
-  if (bh >= a.BH || pair >= pairs) return;
+  const int32_t* counts = a.plan + a.BH * 9;
+  if (local >= counts[xcd]) return;
+  const int2 item = reinterpret_cast<const int2*>(a.plan + attn_plan_list_offset(a.BH))
+      [int64_t(xcd) * a.BH * pairs_per_xcd + local];
+  const int bh = item.x, pair = item.y;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -697,6 +702,138 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   }
 }
 
+// Work-balanced split of each head's query-block pairs over the 8 XCDs.  The
+// work of pair p is the number of key blocks in the union of its two mask
+// rows (bitmap popcount) plus two blocks of set-up; the split points are
+// where the running sum crosses x/8 of the total, clamped so that no range
+// exceeds max_len and the ranges always cover all pairs.  One workgroup per
+// head; two passes over the bitmap rows (total, then split points).
+__global__ __launch_bounds__(256) void plan_kernel(const uint32_t* __restrict__ bitmap,
+                                                   const int32_t* __restrict__ head_mask, int n_masks,
+                                                   int n_qb, int W, int pairs, int max_len,
+                                                   int32_t* __restrict__ plan) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  int mask_id = head_mask ? head_mask[bh] : bh % n_masks;
+  mask_id = min(max(mask_id, 0), n_masks - 1);
+  const uint32_t* bm = bitmap + int64_t(mask_id) * n_qb * W;
+  __shared__ long long part[256];
+  __shared__ int split[9];
+  auto work = [&](int p) -> long long {
+    const uint32_t* r0 = bm + int64_t(2 * p) * W;
+    const bool two = 2 * p + 1 < n_qb;
+    long long c = 2;
+    for (int w = 0; w < W; ++w) c += __builtin_popcount(r0[w] | (two ? r0[W + w] : 0u));
+    return c;
+  };
+  // pass 1: total work
+  long long mine = 0;
+  for (int p = tid; p < pairs; p += 256) mine += work(p);
+  part[tid] = mine;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
+    __syncthreads();
+  }
+  const long long total = part[0];
+  __syncthreads();
+  // pass 2: chunks of 256 consecutive pairs; thread 0 scans each chunk in order
+  if (tid < 9) split[tid] = tid == 0 ? 0 : pairs;
+  long long run = 0;   // work of the pairs before this chunk (valid in thread 0)
+  int next = 1;        // next split point to find (thread 0)
+  for (int base = 0; base < pairs; base += 256) {
+    const int p = base + tid;
+    part[tid] = p < pairs ? work(p) : 0;
+    __syncthreads();
+    if (tid == 0) {
+      for (int i = 0; i < 256 && base + i < pairs && next < 8; ++i) {
+        // split x lies at the first pair whose preceding work reaches x/8
+        while (next < 8 && run * 8 >= total * next) split[next++] = base + i;
+        run += part[i];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    for (int x = 1; x < 8; ++x) {
+      const int lo = max(split[x - 1], pairs - (8 - x) * max_len);
+      const int hi = min(split[x - 1] + max_len, pairs);
+      split[x] = min(max(split[x], lo), hi);
+    }
+    split[8] = pairs;
+    for (int x = 0; x < 9; ++x) plan[bh * 9 + x] = split[x];
+  }
+}
+
+// Work list of each XCD: the ranges plan_kernel gave it, head after head,
+// stably partitioned so that heavy pairs (more than half of all key blocks in
+// the union of their two rows, e.g. the dense rows of text queries) come
+// first and start early.  One workgroup per XCD.
+__global__ __launch_bounds__(256) void order_kernel(const uint32_t* __restrict__ bitmap,
+                                                    const int32_t* __restrict__ head_mask, int n_masks,
+                                                    int n_qb, int n_kb, int W, int BH, int cap,
+                                                    int32_t* __restrict__ plan) {
+  const int x = blockIdx.x, tid = threadIdx.x;
+  const int32_t* split = plan;
+  int32_t* counts = plan + BH * 9;
+  int2* list = reinterpret_cast<int2*>(plan + attn_plan_list_offset(BH)) + int64_t(x) * cap;
+  __shared__ int total_s, heavy_s;
+  __shared__ int scan[256];
+  if (tid == 0) {
+    int t = 0;
+    for (int h = 0; h < BH; ++h) t += split[h * 9 + x + 1] - split[h * 9 + x];
+    total_s = t;
+  }
+  __syncthreads();
+  const int total = total_s;
+  const int chunk = (total + 255) / 256;
+  const int g0 = min(tid * chunk, total), g1 = min(g0 + chunk, total);
+  // walks items g0..g1-1 (head-major order), calling f(h, pair)
+  auto walk = [&](auto f) {
+    int h = 0, base = 0;
+    while (h < BH && base + (split[h * 9 + x + 1] - split[h * 9 + x]) <= g0) {
+      base += split[h * 9 + x + 1] - split[h * 9 + x];
+      ++h;
+    }
+    for (int g = g0; g < g1; ++g) {
+      while (g - base >= split[h * 9 + x + 1] - split[h * 9 + x]) {
+        base += split[h * 9 + x + 1] - split[h * 9 + x];
+        ++h;
+      }
+      f(h, split[h * 9 + x] + (g - base));
+    }
+  };
+  auto heavy = [&](int h, int p) -> bool {
+    int mask_id = head_mask ? head_mask[h] : h % n_masks;
+    mask_id = min(max(mask_id, 0), n_masks - 1);
+    const uint32_t* r0 = bitmap + (int64_t(mask_id) * n_qb + 2 * p) * W;
+    const bool two = 2 * p + 1 < n_qb;
+    int c = 0;
+    for (int w = 0; w < W; ++w) c += __builtin_popcount(r0[w] | (two ? r0[W + w] : 0u));
+    return 2 * c > n_kb;
+  };
+  int mine = 0;
+  walk([&](int h, int p) { mine += heavy(h, p); });
+  scan[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int c = scan[t];
+      scan[t] = run;
+      run += c;
+    }
+    heavy_s = run;
+  }
+  __syncthreads();
+  int hp = scan[tid];                      // next heavy slot
+  int np = heavy_s + (g0 - scan[tid]);     // next normal slot
+  walk([&](int h, int p) {
+    if (heavy(h, p)) list[hp++] = make_int2(h, p);
+    else list[np++] = make_int2(h, p);
+  });
+  if (tid == 0) counts[x] = total;
+}
+
 // V of every head, transposed per 128-key block into the workspace
 // ([bh][kb][d][128], keys past N zero), so the attention kernel can stage V^T
 // tiles with plain 16-byte copies and read the PV operand with ds_read_b128.
@@ -738,7 +875,12 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.vp),
                      a.head_layout, static_cast<__bf16*>(a.vt), a.N, a.n_kb);
   const int pairs = (a.n_qb + 1) / 2;
-  const int per_xcd = (pairs + 7) / 8;
+  const int per_xcd = plan_range_cap(pairs);
+  const int W = (a.n_kb + 31) / 32;
+  hipLaunchKernelGGL(plan_kernel, dim3(a.BH), dim3(256), 0, st, a.bitmap, a.head_mask, a.n_masks,
+                     a.n_qb, W, pairs, per_xcd, a.plan);
+  hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.bitmap, a.head_mask, a.n_masks,
+                     a.n_qb, a.n_kb, W, a.BH, a.BH * per_xcd, a.plan);
   dim3 grid(8 * per_xcd * a.BH);
   hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), grid, dim3(512), 0, st, a, pairs, per_xcd);
 }
@@ -747,7 +889,8 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
 
 size_t attn_workspace_bytes(int BH, int N, int D, int block) {
   if (block != 128) return 0;
-  return size_t(BH) * ceil_div(N, 128) * 128 * D * 2;
+  const int pairs = (ceil_div(N, 128) + 1) / 2;
+  return size_t(BH) * ceil_div(N, 128) * 128 * D * 2 + attn_plan_bytes(BH, pairs);
 }
 
 void launch_attn(const AttnArgs& a, hipStream_t st) {

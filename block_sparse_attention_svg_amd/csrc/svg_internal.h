@@ -61,8 +61,25 @@ struct AttnArgs {
   int BH, N, D, block;
   float scale_log2;  // softmax scale times log2(e)
   void* vt;          // workspace: V of every head, block-transposed (128-key blocks)
+  int32_t* plan;     // workspace: per head, 9 pair indices splitting its pairs over the XCDs
+  const uint32_t* bitmap;  // [n_masks][n_qb][ceil(n_kb/32)]
 };
 size_t attn_workspace_bytes(int BH, int N, int D, int block);
+// Longest range of query-block pairs one XCD may take of a head: 1.5x the
+// even split (edge rows of banded masks carry less work), at least the even
+// split itself.
+__host__ __device__ inline int plan_range_cap(int pairs) {
+  const int a = (3 * pairs + 15) / 16, b = (pairs + 7) / 8;
+  return a > b ? a : b;
+}
+// Bytes of the work plan at the end of the attention workspace: 9 split
+// points per head, 8 list lengths, then 8 work lists of (head, pair) int32
+// pairs, each of capacity BH * plan_range_cap(pairs).
+// int32 offset of the work lists in the plan (8-byte aligned)
+__host__ __device__ inline size_t attn_plan_list_offset(int BH) { return (size_t(BH) * 9 + 8 + 1) & ~size_t(1); }
+inline size_t attn_plan_bytes(int BH, int pairs) {
+  return attn_plan_list_offset(BH) * 4 + size_t(8) * BH * plan_range_cap(pairs) * 8;
+}
 void launch_attn(const AttnArgs& a, hipStream_t st);
 
 struct ProfileArgs {

@@ -152,10 +152,17 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  *   lse            : device float [B,H,N] out (natural-log log-sum-exp of the
  *                    scaled logits, in the layout the head attends in), or NULL.
  *   workspace      : device scratch of >= svg_attn_workspace_bytes(s) bytes
- *                    (V re-laid out per key block); may be NULL when that is 0.
- * A query block whose mask row is empty gets o = 0 and lse = -inf.  The
- * softmax denominator sums the same bf16-rounded weights as the PV product.
- * bf16 inputs, fp32 accumulation and softmax, bf16 output. */
+ *                    (V re-laid out per key block, then a plan that splits
+ *                    every head's query-block pairs over the 8 XCDs into
+ *                    ranges of equal work, from the mask bitmap); 16-byte
+ *                    aligned; may be NULL when the size is 0.  Its contents
+ *                    need no initialisation and are overwritten by every call.
+ * The masks' bitmap and skip list must describe the same mask (as
+ * svg_encode_mask writes them): the kernel walks the skip list and uses the
+ * bitmap to balance work.  A query block whose mask row is empty gets o = 0
+ * and lse = -inf.  bf16 inputs, fp32 accumulation and softmax, bf16 output
+ * (P rounded to bf16 for the PV product; the softmax denominator sums the
+ * fp32 weights). */
 svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,
@@ -163,9 +170,11 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
                                  float* lse, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
-/* Workspace bytes svg_block_sparse_attn needs for shape s (host function):
- * B*H*ceil(N/128)*128*D*2 for 128-token blocks (V transposed per key block),
- * 0 for 64-token blocks. */
+/* Workspace bytes svg_block_sparse_attn needs for shape s (host function).
+ * 128-token blocks: B*H*ceil(N/128)*128*D*2 (V transposed per key block), then
+ * a work plan of (9*B*H + 8 rounded up to even)*4 + 8*B*H*cap*8 bytes with
+ * pairs = ceil(ceil(N/128)/2) and cap = max(ceil(3*pairs/16), ceil(pairs/8)).
+ * 64-token blocks: 0. */
 size_t svg_attn_workspace_bytes(svg_shape s);
 
 /* ---- a7: row-repetitive heads ------------------------------------------- */
