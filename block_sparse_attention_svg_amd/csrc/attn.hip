@@ -702,12 +702,40 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   }
 }
 
-// Work-balanced split of each head's query-block pairs over the 8 XCDs.  The
-// work of pair p is the number of key blocks in the union of its two mask
-// rows (bitmap popcount) plus two blocks of set-up; the split points are
-// where the running sum crosses x/8 of the total, clamped so that no range
-// exceeds max_len and the ranges always cover all pairs.  One workgroup per
-// head; two passes over the bitmap rows (total, then split points).
+// Work of query-block pair p of a mask: key blocks in the union of its two
+// rows (bitmap popcount) plus two blocks of set-up.
+__device__ __forceinline__ int pair_work(const uint32_t* __restrict__ bm, int p, int n_qb, int W) {
+  const uint32_t* r0 = bm + int64_t(2 * p) * W;
+  const bool two = 2 * p + 1 < n_qb;
+  int c = 2;
+  for (int w = 0; w < W; ++w) c += __builtin_popcount(r0[w] | (two ? r0[W + w] : 0u));
+  return c;
+}
+
+// Inclusive scan of one value per thread over a 256-thread workgroup; every
+// thread also gets the workgroup total.
+__device__ __forceinline__ long long block_scan256(long long v, long long* tmp, long long& total) {
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int off = 1; off < 256; off <<= 1) {
+    const long long add = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const long long r = tmp[tid];
+  total = tmp[255];
+  __syncthreads();
+  return r;
+}
+
+// Work-balanced split of each head's query-block pairs over the 8 XCDs: split
+// x (1..7) is the first pair whose preceding work reaches x/8 of the head's
+// total, then clamped so that no range exceeds max_len and the ranges always
+// cover all pairs.  One workgroup per head; pairs in chunks of 256, each
+// thread checks whether a split point falls on its pair.
 __global__ __launch_bounds__(256) void plan_kernel(const uint32_t* __restrict__ bitmap,
                                                    const int32_t* __restrict__ head_mask, int n_masks,
                                                    int n_qb, int W, int pairs, int max_len,
@@ -716,43 +744,36 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint32_t* __restrict__ 
   int mask_id = head_mask ? head_mask[bh] : bh % n_masks;
   mask_id = min(max(mask_id, 0), n_masks - 1);
   const uint32_t* bm = bitmap + int64_t(mask_id) * n_qb * W;
-  __shared__ long long part[256];
+  __shared__ long long tmp[256];
   __shared__ int split[9];
-  auto work = [&](int p) -> long long {
-    const uint32_t* r0 = bm + int64_t(2 * p) * W;
-    const bool two = 2 * p + 1 < n_qb;
-    long long c = 2;
-    for (int w = 0; w < W; ++w) c += __builtin_popcount(r0[w] | (two ? r0[W + w] : 0u));
-    return c;
-  };
-  // pass 1: total work
-  long long mine = 0;
-  for (int p = tid; p < pairs; p += 256) mine += work(p);
-  part[tid] = mine;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) part[tid] += part[tid + off];
-    __syncthreads();
-  }
-  const long long total = part[0];
-  __syncthreads();
-  // pass 2: chunks of 256 consecutive pairs; thread 0 scans each chunk in order
   if (tid < 9) split[tid] = tid == 0 ? 0 : pairs;
-  long long run = 0;   // work of the pairs before this chunk (valid in thread 0)
-  int next = 1;        // next split point to find (thread 0)
+  // pass 1: work of every pair (kept for order_kernel) and the total
+  int32_t* work = plan + attn_plan_work_offset(gridDim.x, pairs) + int64_t(bh) * pairs;
+  long long mine = 0;
+  for (int p = tid; p < pairs; p += 256) {
+    const int w = pair_work(bm, p, n_qb, W);
+    work[p] = w;
+    mine += w;
+  }
+  long long T = 0;
+  block_scan256(mine, tmp, T);   // its barriers also publish work[]
+  // pass 2: split points (excl = work of the pairs before p)
+  long long carry = 0;
   for (int base = 0; base < pairs; base += 256) {
     const int p = base + tid;
-    part[tid] = p < pairs ? work(p) : 0;
-    __syncthreads();
-    if (tid == 0) {
-      for (int i = 0; i < 256 && base + i < pairs && next < 8; ++i) {
-        // split x lies at the first pair whose preceding work reaches x/8
-        while (next < 8 && run * 8 >= total * next) split[next++] = base + i;
-        run += part[i];
-      }
+    const long long w = p < pairs ? work[p] : 0;
+    long long chunk = 0;
+    const long long excl = carry + block_scan256(w, tmp, chunk) - w;
+    if (p < pairs) {
+      // p is split x iff excl(p) >= x T / 8 > excl(p - 1) = excl(p) - work(p - 1)
+      const long long wprev = p == 0 ? 0 : work[p - 1];
+      for (int x = 1; x < 8; ++x)
+        if (excl * 8 >= T * x && (p == 0 || (excl - wprev) * 8 < T * x)) split[x] = p;
     }
+    carry += chunk;
     __syncthreads();
   }
+  __syncthreads();
   if (tid == 0) {
     for (int x = 1; x < 8; ++x) {
       const int lo = max(split[x - 1], pairs - (8 - x) * max_len);
@@ -768,26 +789,21 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint32_t* __restrict__ 
 // stably partitioned so that heavy pairs (more than half of all key blocks in
 // the union of their two rows, e.g. the dense rows of text queries) come
 // first and start early.  One workgroup per XCD.
-__global__ __launch_bounds__(256) void order_kernel(const uint32_t* __restrict__ bitmap,
-                                                    const int32_t* __restrict__ head_mask, int n_masks,
-                                                    int n_qb, int n_kb, int W, int BH, int cap,
+__global__ __launch_bounds__(256) void order_kernel(int n_kb, int BH, int pairs, int cap,
                                                     int32_t* __restrict__ plan) {
   const int x = blockIdx.x, tid = threadIdx.x;
   const int32_t* split = plan;
   int32_t* counts = plan + BH * 9;
   int2* list = reinterpret_cast<int2*>(plan + attn_plan_list_offset(BH)) + int64_t(x) * cap;
-  __shared__ int total_s, heavy_s;
-  __shared__ int scan[256];
-  if (tid == 0) {
-    int t = 0;
-    for (int h = 0; h < BH; ++h) t += split[h * 9 + x + 1] - split[h * 9 + x];
-    total_s = t;
-  }
-  __syncthreads();
-  const int total = total_s;
+  __shared__ long long tmp[256];
+  // items of this XCD, head-major: item g of head h is pair split[h][x] + g - base(h)
+  long long len_sum = 0;
+  for (int h = tid; h < BH; h += 256) len_sum += split[h * 9 + x + 1] - split[h * 9 + x];
+  long long total_ll = 0;
+  block_scan256(len_sum, tmp, total_ll);
+  const int total = int(total_ll);
   const int chunk = (total + 255) / 256;
   const int g0 = min(tid * chunk, total), g1 = min(g0 + chunk, total);
-  // walks items g0..g1-1 (head-major order), calling f(h, pair)
   auto walk = [&](auto f) {
     int h = 0, base = 0;
     while (h < BH && base + (split[h * 9 + x + 1] - split[h * 9 + x]) <= g0) {
@@ -802,34 +818,26 @@ __global__ __launch_bounds__(256) void order_kernel(const uint32_t* __restrict__
       f(h, split[h * 9 + x] + (g - base));
     }
   };
-  auto heavy = [&](int h, int p) -> bool {
-    int mask_id = head_mask ? head_mask[h] : h % n_masks;
-    mask_id = min(max(mask_id, 0), n_masks - 1);
-    const uint32_t* r0 = bitmap + (int64_t(mask_id) * n_qb + 2 * p) * W;
-    const bool two = 2 * p + 1 < n_qb;
-    int c = 0;
-    for (int w = 0; w < W; ++w) c += __builtin_popcount(r0[w] | (two ? r0[W + w] : 0u));
-    return 2 * c > n_kb;
-  };
-  int mine = 0;
-  walk([&](int h, int p) { mine += heavy(h, p); });
-  scan[tid] = mine;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int c = scan[t];
-      scan[t] = run;
-      run += c;
-    }
-    heavy_s = run;
-  }
-  __syncthreads();
-  int hp = scan[tid];                      // next heavy slot
-  int np = heavy_s + (g0 - scan[tid]);     // next normal slot
+  const int32_t* work = plan + attn_plan_work_offset(BH, pairs);
+  auto heavy = [&](int h, int p) -> bool { return 2 * (work[int64_t(h) * pairs + p] - 2) > n_kb; };
+  uint64_t flags = 0;   // heavy flags of this thread's items (chunk <= 64), else recomputed
+  int mine = 0, i = 0;
   walk([&](int h, int p) {
-    if (heavy(h, p)) list[hp++] = make_int2(h, p);
+    const bool hv = heavy(h, p);
+    if (i < 64 && hv) flags |= uint64_t(1) << i;
+    mine += hv;
+    ++i;
+  });
+  long long heavy_total = 0;
+  const int hp0 = int(block_scan256(mine, tmp, heavy_total)) - mine;
+  int hp = hp0;                                   // next heavy slot
+  int np = int(heavy_total) + (g0 - hp0);         // next normal slot
+  i = 0;
+  walk([&](int h, int p) {
+    const bool hv = i < 64 ? ((flags >> i) & 1) != 0 : heavy(h, p);
+    if (hv) list[hp++] = make_int2(h, p);
     else list[np++] = make_int2(h, p);
+    ++i;
   });
   if (tid == 0) counts[x] = total;
 }
@@ -879,8 +887,8 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
   const int W = (a.n_kb + 31) / 32;
   hipLaunchKernelGGL(plan_kernel, dim3(a.BH), dim3(256), 0, st, a.bitmap, a.head_mask, a.n_masks,
                      a.n_qb, W, pairs, per_xcd, a.plan);
-  hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.bitmap, a.head_mask, a.n_masks,
-                     a.n_qb, a.n_kb, W, a.BH, a.BH * per_xcd, a.plan);
+  hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.n_kb, a.BH, pairs, a.BH * per_xcd,
+                     a.plan);
   dim3 grid(8 * per_xcd * a.BH);
   hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), grid, dim3(512), 0, st, a, pairs, per_xcd);
 }

@@ -172,9 +172,9 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
 
 /* Workspace bytes svg_block_sparse_attn needs for shape s (host function).
  * 128-token blocks: B*H*ceil(N/128)*128*D*2 (V transposed per key block), then
- * a work plan of (9*B*H + 8 rounded up to even)*4 + 8*B*H*cap*8 bytes with
- * pairs = ceil(ceil(N/128)/2) and cap = max(ceil(3*pairs/16), ceil(pairs/8)).
- * 64-token blocks: 0. */
+ * a work plan of (9*B*H + 8 rounded up to even)*4 + 8*B*H*cap*8 + B*H*pairs*4
+ * bytes with pairs = ceil(ceil(N/128)/2) and cap = max(ceil(3*pairs/16),
+ * ceil(pairs/8)).  64-token blocks: 0. */
 size_t svg_attn_workspace_bytes(svg_shape s);
 
 /* ---- a7: row-repetitive heads ------------------------------------------- */
