@@ -275,12 +275,14 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_fwd_kernel(AttnArgs a) {
 // of S_{j-1}; phase 2 swaps the roles.  The two waves sharing a SIMD thus
 // alternate between matrix work and VALU work; one barrier per block (at its
 // end) orders the buffer refills.  K_j and V^T_j land in
-// double-buffered LDS through 16-byte global->LDS copies issued by the group
-// doing softmax: V^T of block j in phase 1 (group 1), K of block j+1 in
-// phase 2 (group 0).  The copies go out before that group's softmax and land
-// while the phase runs; the waves running MFMAs never issue one.  V^T comes
+// double-buffered LDS through 16-byte global->LDS copies, all issued by
+// group 0 in phase 2 (K of block j+1, V^T of block j), before its softmax:
+// group 1 then runs MFMAs whose operand reads no longer compete with fresh
+// copies for the LDS, and the waves running MFMAs never issue one.  V^T comes
 // from a per-block transposed workspace, so both operands are read with
-// plain 16-byte LDS fetches.
+// plain 16-byte LDS fetches.  The merged key-block sequence of the two rows
+// is built in LDS once per 2048 key blocks, so choosing the next block is
+// one LDS read.
 // ---------------------------------------------------------------------------
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -359,47 +361,61 @@ struct Cfg2 {
   }
 };
 
-// One mask row's skip list held in registers: lane l holds interval t0 + l
-// (clamped to [0, nKB); lanes past the row's end hold an empty interval).
-// Rows with more than 64 intervals are walked one 64-interval window at a
-// time.  Intervals of a row are ascending and disjoint, as the encoder emits
-// them.
-struct IvWindow {
-  int t0, r1;   // first interval of the window, end of the row's intervals
-  int s, e;     // this lane's interval
+// The merged key-block sequence of a workgroup's two mask rows, built in LDS
+// one window of 64 bitmap words (2048 key blocks) at a time: the rows'
+// skip-list intervals clipped to the window are expanded into two 64-word
+// bitmaps, then one wave lists the set bits of their union in order (prefix
+// sum of the word popcounts).  Entry: key block in bits 0-29, bit 30 / 31 set
+// when row 0 / row 1 keeps it; the window ends with kSeqRefill (more words
+// follow) or kSeqEnd.
+constexpr int kSeqWords = 64, kSeqCap = 32 * kSeqWords + 1;
+constexpr uint32_t kSeqEnd = 0x3fffffffu, kSeqRefill = 0x3ffffffeu;
+
+struct SeqLds {
+  uint32_t bits[2][kSeqWords];
+  uint32_t seq[kSeqCap];
 };
 
-__device__ __forceinline__ void iv_window_load(IvWindow& w, const int32_t* __restrict__ iv, int t0,
-                                               int nKB) {
-  w.t0 = t0;
-  const int t = t0 + (threadIdx.x & 63);
-  w.s = 0;
-  w.e = 0;
-  if (t < w.r1) {
-    w.s = max(iv[2 * t], 0);
-    w.e = min(iv[2 * t + 1], nKB);
-  }
-}
-
-__device__ __forceinline__ void iv_row_start(IvWindow& w, const int32_t* __restrict__ row_ptr,
-                                             const int32_t* __restrict__ iv, int row, bool exists,
-                                             int nKB) {
-  w.r1 = exists ? row_ptr[row + 1] : 0;
-  iv_window_load(w, iv, exists ? row_ptr[row] : 0, nKB);
-}
-
-// Smallest kept block >= x of the row, or INT_MAX.  x only grows between
-// calls, so windows are consumed in order.
-__device__ __forceinline__ int iv_next(IvWindow& w, const int32_t* __restrict__ iv, int x, int nKB) {
-  for (;;) {
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(w.e > x && w.s < w.e);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      return max(__builtin_amdgcn_readlane(w.s, l), x);
+// Builds window w; every thread of the workgroup calls it (it synchronizes).
+__device__ __forceinline__ void seq_build(SeqLds& L, const int32_t* __restrict__ row_ptr,
+                                          const int32_t* __restrict__ iv, int row0, bool two,
+                                          int nKB, int w) {
+  const int tid = threadIdx.x;
+  const int W = (nKB + 31) >> 5;
+  const int kb0 = 32 * kSeqWords * w, kb1 = min(kb0 + 32 * kSeqWords, nKB);
+  __syncthreads();   // the previous window is no longer read
+  if (tid < 2 * kSeqWords) L.bits[tid / kSeqWords][tid % kSeqWords] = 0u;
+  __syncthreads();
+  for (int r = 0; r < (two ? 2 : 1); ++r) {
+    const int t1 = row_ptr[row0 + r + 1];
+    for (int t = row_ptr[row0 + r] + tid; t < t1; t += blockDim.x) {
+      const int s = max(iv[2 * t], kb0) - kb0, e = min(iv[2 * t + 1], kb1) - kb0;
+      for (int q = s >> 5; s < e && q <= (e - 1) >> 5; ++q) {
+        const int lo = max(s - 32 * q, 0), hi = min(e - 32 * q, 32);
+        const uint32_t m = (hi == 32 ? ~0u : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+        atomicOr(&L.bits[r][q], m);
+      }
     }
-    if (w.t0 + 64 >= w.r1) return INT_MAX;
-    iv_window_load(w, iv, w.t0 + 64, nKB);
   }
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t a = L.bits[0][tid], b = L.bits[1][tid], u = a | b;
+    const int c = __builtin_popcount(u);
+    int incl = c;   // inclusive prefix sum over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (tid >= off) incl += y;
+    }
+    int o = incl - c;
+    for (uint32_t x = u; x; x &= x - 1) {
+      const int bit = __builtin_ctz(x);
+      L.seq[o++] = uint32_t(kb0 + 32 * tid + bit) | (((a >> bit) & 1u) << 30) | (((b >> bit) & 1u) << 31);
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (tid == 0) L.seq[total] = (w + 1) * kSeqWords < W ? kSeqRefill : kSeqEnd;
+  }
+  __syncthreads();
 }
 
 // S^T (128 keys x 32 queries) = K Q^T.  The scheduling barriers keep the K
@@ -459,6 +475,13 @@ __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf
   }
 }
 
+// max of x over lanes l and l ^ 32 (one VALU swap of the wave halves, no LDS)
+__device__ __forceinline__ float max_cross_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 // Online softmax of one 128-key block: S (raw logits) -> P (bf16), updating the
 // running max m (log2 units, moved only when the block max exceeds it by more
 // than 2^8), the lane's share of the denominator and, on a move, O.
@@ -480,7 +503,7 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
   for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-  mx = fmaxf(mx, shfl_xor_f(mx, 32)) * c2;
+  mx = max_cross_half(mx) * c2;
   if (mx > m_run + kRescaleLog2) {
     const float alpha = fast_exp2(m_run - mx);
     l_part *= alpha;
@@ -596,18 +619,24 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   f32x16 sacc[C::KT];
   bf16x8 pb[C::PS];
 
-  IvWindow wa, wb;
-  iv_row_start(wa, a.row_ptr, a.iv, mask_id * a.n_qb + qb0, true, a.n_kb);
-  iv_row_start(wb, a.row_ptr, a.iv, mask_id * a.n_qb + qb0 + 1, has_b, a.n_kb);
-  int na = iv_next(wa, a.iv, 0, a.n_kb), nb = iv_next(wb, a.iv, 0, a.n_kb);
-  // merged block sequence of the two rows; `mine` = the block is in my row
+  __shared__ SeqLds sl;
+  const int row0 = mask_id * a.n_qb + qb0;
+  int seq_w = 0, seq_j = 1;
+  seq_build(sl, a.row_ptr, a.iv, row0, has_b, a.n_kb, 0);
+  uint32_t seq_v = sl.seq[0];   // next entry, read one call ahead
+  // Next block of the merged sequence; `mine` = my row keeps it.  All waves
+  // call this at the same points, so a window refill may synchronize.
   auto pick = [&](int& kb, bool& mine) -> bool {
-    kb = min(na, nb);
-    if (kb == INT_MAX) return false;
-    const bool in_a = na == kb, in_b = nb == kb;
-    if (in_a) na = iv_next(wa, a.iv, kb + 1, a.n_kb);
-    if (in_b) nb = iv_next(wb, a.iv, kb + 1, a.n_kb);
-    mine = grp == 0 ? in_a : in_b;
+    uint32_t e = __builtin_amdgcn_readfirstlane(seq_v);
+    if ((e & 0x3fffffffu) == kSeqRefill) {
+      seq_build(sl, a.row_ptr, a.iv, row0, has_b, a.n_kb, ++seq_w);
+      e = __builtin_amdgcn_readfirstlane(sl.seq[0]);
+      seq_j = 1;
+    }
+    kb = int(e & 0x3fffffffu);
+    if (kb == int(kSeqEnd)) return false;
+    seq_v = sl.seq[seq_j++];
+    mine = grp == 0 ? (e >> 30) & 1u : (e >> 31) & 1u;
     return true;
   };
 
@@ -640,9 +669,6 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
       if (have_prev && mine_prev) mfma_pv<D>(v_prev, v_lane, pb, oacc);
       if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
     } else {
-      // V^T of block j into the V buffer freed by block j-2
-      copy_v(v_src(kb_cur, have_cur), vb_lds[kbuf]);
-      __builtin_amdgcn_sched_barrier(0);
       if (have_prev && mine_prev)
         softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_prev * C::BLK, N, h, c2);
     }
@@ -653,8 +679,11 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
     __builtin_amdgcn_sched_barrier(0);
     // ---- phase 2 --------------------------------------------------------------
     if (grp == 0) {
-      // K of block j+1 into the K buffer freed by block j-1
+      // K of block j+1 into the K buffer freed by block j-1, V^T of block j
+      // into the V buffer freed by block j-2
       copy_k(k_src(kb_next, have_next), kb_lds[kbuf ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      copy_v(v_src(kb_cur, have_cur), vb_lds[kbuf]);
       __builtin_amdgcn_sched_barrier(0);
       if (have_cur && mine_cur)
         softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_cur * C::BLK, N, h, c2);

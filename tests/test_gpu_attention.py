@@ -189,3 +189,39 @@ def test_batch2_heavy_and_empty_rows_over_many_pairs():
             ref, _ = O.block_masked_attention(q[b, h].float().numpy(), k[b, h].float().numpy(),
                                               v[b, h].float().numpy(), masks[b * w.H + h], 128, w.scale)
             assert_attn_close(to_np(o[b, h]), ref, f"batch {b} head {h}")
+
+
+def test_long_rows_cross_block_list_windows():
+    """More than 2048 key blocks: the kernel lists a pair's kept blocks in
+    windows of 2048.  Rows whose kept blocks straddle, precede or follow the
+    window boundary (also within one pair), a dense ragged last row and
+    random sparse rows, sampled against the oracle."""
+    banner("attn long rows")
+    w = S.get_workload("tiny", F=7, Hs=160, Ws=240, text=5, H=2, D=64)   # N = 268805: 2101 blocks
+    q, k, v, _ = S.gen_qkv(w, dtype="bf16")
+    nB = -(-w.N // 128)
+    rng = np.random.default_rng(13)
+    masks = (rng.random((2, nB, nB)) < 0.02).astype(np.uint8)
+    masks[0, 10, 2000:2100] = 1                    # a run across the boundary
+    masks[0, 11] = 0
+    masks[0, 11, 2049:] = 1                        # its pair partner: only after it
+    masks[1, 20] = 0
+    masks[1, 20, :2048] = 1                        # pair (20, 21): before / after
+    masks[1, 21] = 0
+    masks[1, 21, 2048:] = 1
+    masks[:, nB - 1] = 1                           # dense ragged last row
+    s = svg.Shape(1, 2, w.N, w.D, w.F, w.Hs, w.Ws, 128)
+    enc = svg.svg_encode_mask(torch.from_numpy(masks).to(DEV))
+    hm = torch.arange(2, dtype=torch.int32, device=DEV)
+    o, _, lse = svg.svg_block_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), s, w.scale, enc,
+                                          head_mask=hm, lse=True)
+    torch.cuda.synchronize()
+    qbs = [0, 10, 11, 20, 21, 1024, nB - 2, nB - 1]
+    for h in range(2):
+        ref, ref_lse = O.block_masked_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                                v[0, h].float().numpy(), masks[h], 128, w.scale,
+                                                qblocks=qbs)
+        rows = ~np.isnan(ref[:, 0])
+        assert_attn_close(to_np(o[0, h])[rows], ref[rows], f"long rows head {h}")
+        g = lse[0, h].cpu().numpy()[rows]
+        assert np.max(np.abs(g - ref_lse[rows])) < LSE_ABS
