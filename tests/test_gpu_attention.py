@@ -225,3 +225,35 @@ def test_long_rows_cross_block_list_windows():
         assert_attn_close(to_np(o[0, h])[rows], ref[rows], f"long rows head {h}")
         g = lse[0, h].cpu().numpy()[rows]
         assert np.max(np.abs(g - ref_lse[rows])) < LSE_ABS
+
+
+@pytest.mark.parametrize("order", ["rising", "falling", "one_spike"])
+def test_softmax_reference_moves(order):
+    """Scores that rise by ~36 (log2 units) per key block move the running
+    max at every block (O and the denominator rescaled each time); falling
+    scores never move it (later weights underflow towards 0); one far larger
+    block moves it once.  All rows, O and LSE, against the oracle."""
+    banner("attn reference", order)
+    N, D, nB = 1000, 64, 8                                  # ragged last block
+    rng = np.random.default_rng(17)
+    u = np.full(D, 0.5)                                     # |u|^2 = 16, q.k = 16 c
+    blk = np.arange(N) // 128
+    c = {"rising": 25.0 * blk, "falling": 25.0 * (nB - 1 - blk),
+         "one_spike": np.where(blk == 5, 60.0, 0.0)}[order]
+    qn = (u[None, :] + 0.05 * rng.standard_normal((N, D)))
+    kn = c[:, None] * u[None, :] / 16.0 * 8.0 + 0.05 * rng.standard_normal((N, D))   # s = c / scale-free
+    vn = rng.standard_normal((N, D))
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).reshape(1, 1, N, D).contiguous() for x in (qn, kn, vn))
+    scale = 1.0 / np.sqrt(D)
+    masks = np.ones((1, nB, nB), dtype=np.uint8)
+    s = svg.Shape(1, 1, N, D, 1, 1, 1, 128)
+    enc = svg.svg_encode_mask(torch.from_numpy(masks).to(DEV))
+    hm = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o, _, lse = svg.svg_block_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), s, scale, enc,
+                                          head_mask=hm, lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.block_masked_attention(q[0, 0].float().numpy(), k[0, 0].float().numpy(),
+                                            v[0, 0].float().numpy(), masks[0], 128, scale)
+    assert np.all(np.isfinite(to_np(o[0, 0])))
+    assert_attn_close(to_np(o[0, 0]), ref, f"reference {order}")
+    assert np.max(np.abs(lse[0, 0].cpu().numpy() - ref_lse)) < LSE_ABS * max(1.0, float(np.max(np.abs(ref_lse))) / 64)
