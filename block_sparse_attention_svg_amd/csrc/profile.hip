@@ -43,7 +43,7 @@ constexpr int kTK = 32;         // keys staged per LDS tile (one 32-key step)
 constexpr int kThreads = 256;
 constexpr int kMaxWords = 32;   // bitmap words per row held in LDS (nB <= 1024)
 constexpr int kChunkKeys = 32768;
-constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleLog2 = 24.0f;   // weights stay below 2^24 between moves
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
@@ -193,16 +193,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int v_lane = C::KCH * 16 + ((8 * grp + (n >> 2)) * C::VROW) * 16 + ((n & 3) * 4) * 2;
   const float c2 = a.scale_log2;
 
+  // Admission of this lane's 8 keys of a tile (8 * grp + i) for its sample:
+  // bit i = kept by the temporal row, bit 8 = the tile's key block kept by
+  // the spatial row.  Computed one tile ahead, so the dependent LDS lookups
+  // overlap the previous tile's MFMAs.
+  auto admission = [&](int key0, int b) -> uint32_t {
+    const int kblock = min(key0 >> g.blk_log2, a.nB - 1);   // one key block for all 32 keys
+    uint32_t bits = (svalid && ((rowS[sidx][kblock >> 5] >> (kblock & 31)) & 1u)) ? 0x100u : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int bt = blkT[b][8 * grp + i];
+      bits |= ((rowT[sidx][bt >> 5] >> (bt & 31)) & 1u) << i;
+    }
+    return bits;
+  };
+
   if (n_tiles > 0) stage(k_begin, 0);
   if (n_tiles > 1) stage(k_begin + kTK, 1);
+  __syncthreads();   // sample rows and the first tile's key blocks are visible
+  uint32_t adm_next = n_tiles > 0 ? admission(k_begin, 0) : 0u;
   for (int t = 0; t < n_tiles; ++t) {
     const int b = t % C::STAGES;
     const int key0 = k_begin + t * kTK;
+    const uint32_t adm = adm_next;
     // this thread's copies of tile t have landed (tile t+1 may still fly)
     if (t + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(0x3f70 | C::SPW);   // vmcnt(SPW)
     else __builtin_amdgcn_s_waitcnt(0x3f70);                            // vmcnt(0)
     barrier_lds();     // everyone's copies landed; stage (t+2)%3 is no longer read
     if (t + 2 < n_tiles) stage(key0 + 2 * kTK, (t + 2) % C::STAGES);
+    if (t + 1 < n_tiles) adm_next = admission(key0 + kTK, (t + 1) % C::STAGES);
     const char* lb = lds_b + b * C::STRIDE * 16;
 #pragma unroll
     for (int half = 0; half < kTK / 32; ++half) {
@@ -218,17 +237,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           s2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(raw), qreg[kk], s2[tile], 0, 0, 0);
         }
       }
-      const int kbase = key0 + half * 32;
-      const int kblock = min(kbase >> g.blk_log2, a.nB - 1);   // one key block for all 32 keys
-      const bool inS = svalid && ((rowS[sidx][kblock >> 5] >> (kblock & 31)) & 1u);
+      const bool inS = (adm >> 8) & 1u;
       float x[8];
       bool inT[8];
       float m_in = -INFINITY, m_out = -INFINITY;   // this lane's max over T-kept / T-skipped keys
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int kl = half * 32 + 8 * grp + i;
-        const int bt = blkT[b][kl];
-        inT[i] = (rowT[sidx][bt >> 5] >> (bt & 31)) & 1u;
+        inT[i] = (adm >> i) & 1u;
         const bool ok = svalid && key0 + kl < k_end;
         x[i] = ok ? s2[i >> 2][i & 3] : -INFINITY;
         m_in = fmaxf(m_in, inT[i] ? x[i] : -INFINITY);
@@ -240,7 +256,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       float r_in = inS ? mrun[0] : mrun[2];
       float r_out = inS ? mrun[1] : mrun[3];
       // Fast path: no lane's block max exceeds its running max by more than
-      // 2^8, so the stale maxima stay valid and no cross-lane exchange is
+      // 2^24, so the stale maxima stay valid and no cross-lane exchange is
       // needed.  Otherwise combine the maxima over the 4 lanes of each sample
       // and rescale the classes whose maximum moved.
       if (__ballot(m_in > r_in + kRescaleLog2 || m_out > r_out + kRescaleLog2)) {
