@@ -333,27 +333,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // Merge the chunks of one (head, sample) and evaluate both masks' errors.
+// Wave c takes class c: the max over the chunks' maxima, each chunk's weight
+// 2^(m_chunk - M) (kept in LDS) and Z; then thread d sums U[d] of every
+// class with those weights.  All sums have a fixed order.
+constexpr int kMergeCache = 512;   // chunk weights held in LDS (more are recomputed)
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, shfl_xor_f(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += shfl_xor_f(x, off);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, double* __restrict__ per_sample) {
   using C = PCfg<D>;
   const int bh = blockIdx.x, sidx = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float M[4];
   __shared__ float Z[4];
-  __shared__ double red[2][256];
+  __shared__ float Wc[4][kMergeCache];
+  __shared__ double red[2][4];
   const float* base = a.ws + (int64_t(bh) * a.n_chunks * kQ + sidx) * 4 * C::REC;
   const int64_t chunk_stride = int64_t(kQ) * 4 * C::REC;
-  if (tid < 4) {
+  const int nc = a.n_chunks;
+  auto weight = [&](int c, int ch, float m) -> float {
+    const float mc = base[ch * chunk_stride + c * C::REC];
+    return (m == -INFINITY || mc == -INFINITY) ? 0.f : fast_exp2(mc - m);
+  };
+  {
+    const int c = wave;
     float m = -INFINITY;
-    for (int ch = 0; ch < a.n_chunks; ++ch) m = fmaxf(m, base[ch * chunk_stride + tid * C::REC]);
+    for (int ch = lane; ch < nc; ch += 64) m = fmaxf(m, base[ch * chunk_stride + c * C::REC]);
+    m = wave_max64(m);
     float z = 0.f;
-    if (m != -INFINITY)
-      for (int ch = 0; ch < a.n_chunks; ++ch) {
-        const float* r = base + ch * chunk_stride + tid * C::REC;
-        if (r[0] != -INFINITY) z += r[1] * fast_exp2(r[0] - m);
-      }
-    M[tid] = m;
-    Z[tid] = z;
+    for (int ch = lane; ch < nc; ch += 64) {
+      const float w = weight(c, ch, m);
+      if (ch < kMergeCache) Wc[c][ch] = w;
+      z += base[ch * chunk_stride + c * C::REC + 1] * w;
+    }
+    z = wave_sum64(z);
+    if (lane == 0) {
+      M[c] = m;
+      Z[c] = z;
+    }
   }
   __syncthreads();
   double e[2] = {0.0, 0.0};
@@ -361,13 +388,17 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, doubl
     float U[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float u = 0.f;
-      if (M[c] != -INFINITY)
-        for (int ch = 0; ch < a.n_chunks; ++ch) {
-          const float* r = base + ch * chunk_stride + c * C::REC;
-          if (r[0] != -INFINITY) u += r[4 + d] * fast_exp2(r[0] - M[c]);
-        }
-      U[c] = u;
+      float u0 = 0.f, u1 = 0.f;
+      const float* r = base + c * C::REC + 4 + d;
+      int ch = 0;
+      for (; ch + 1 < nc; ch += 2) {
+        const float w0 = ch < kMergeCache ? Wc[c][ch] : weight(c, ch, M[c]);
+        const float w1 = ch + 1 < kMergeCache ? Wc[c][ch + 1] : weight(c, ch + 1, M[c]);
+        u0 += r[ch * chunk_stride] * w0;
+        u1 += r[(ch + 1) * chunk_stride] * w1;
+      }
+      if (ch < nc) u0 += r[ch * chunk_stride] * (ch < kMergeCache ? Wc[c][ch] : weight(c, ch, M[c]));
+      U[c] = u0 + u1;
     }
 #pragma unroll
     for (int mask = 0; mask < 2; ++mask) {
@@ -398,19 +429,20 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, doubl
       e[mask] += double(diff) * double(diff);
     }
   }
-  red[0][tid] = e[0];
-  red[1][tid] = e[1];
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) {
-      red[0][tid] += red[0][tid + off];
-      red[1][tid] += red[1][tid + off];
-    }
-    __syncthreads();
+  // fixed-order sum: lanes of a wave by a butterfly, then the four waves in order
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) e[k] += __shfl_xor(e[k], off, 64);
   }
+  if (lane == 0) {
+    red[0][wave] = e[0];
+    red[1][wave] = e[1];
+  }
+  __syncthreads();
   if (tid == 0) {
-    per_sample[(int64_t(bh) * kQ + sidx) * 2 + 0] = red[0][0];
-    per_sample[(int64_t(bh) * kQ + sidx) * 2 + 1] = red[1][0];
+    per_sample[(int64_t(bh) * kQ + sidx) * 2 + 0] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+    per_sample[(int64_t(bh) * kQ + sidx) * 2 + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
   }
 }
 
