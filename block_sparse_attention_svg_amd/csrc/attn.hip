@@ -361,45 +361,33 @@ struct Cfg2 {
   }
 };
 
-// The merged key-block sequence of a workgroup's two mask rows, built in LDS
-// one window of 64 bitmap words (2048 key blocks) at a time: the rows'
-// skip-list intervals clipped to the window are expanded into two 64-word
-// bitmaps, then one wave lists the set bits of their union in order (prefix
-// sum of the word popcounts).  Entry: key block in bits 0-29, bit 30 / 31 set
-// when row 0 / row 1 keeps it; the window ends with kSeqRefill (more words
-// follow) or kSeqEnd.
+// The merged key-block sequence of a workgroup's two mask rows (the skip list
+// of their union), built in LDS one window of 64 bitmap words (2048 key
+// blocks) at a time: one wave reads the two rows' bitmap words of the window
+// (a single load each, no chain of dependent loads through the interval
+// list) and lists the set bits of their union in order (prefix sum of the
+// word popcounts).  Entry: key block in bits 0-29, bit 30 / 31 set when row 0
+// / row 1 keeps it; the window ends with kSeqRefill (more words follow) or
+// kSeqEnd.
 constexpr int kSeqWords = 64, kSeqCap = 32 * kSeqWords + 1;
 constexpr uint32_t kSeqEnd = 0x3fffffffu, kSeqRefill = 0x3ffffffeu;
 
 struct SeqLds {
-  uint32_t bits[2][kSeqWords];
   uint32_t seq[kSeqCap];
 };
 
-// Builds window w; every thread of the workgroup calls it (it synchronizes).
-__device__ __forceinline__ void seq_build(SeqLds& L, const int32_t* __restrict__ row_ptr,
-                                          const int32_t* __restrict__ iv, int row0, bool two,
-                                          int nKB, int w) {
+// Builds window w from the bitmap rows bm0 (row 0) and bm0 + W (row 1, read
+// only when `two`); every thread of the workgroup calls it (it synchronizes).
+__device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict__ bm0, bool two,
+                                          int W, int w) {
   const int tid = threadIdx.x;
-  const int W = (nKB + 31) >> 5;
-  const int kb0 = 32 * kSeqWords * w, kb1 = min(kb0 + 32 * kSeqWords, nKB);
+  const int kb0 = 32 * kSeqWords * w;
   __syncthreads();   // the previous window is no longer read
-  if (tid < 2 * kSeqWords) L.bits[tid / kSeqWords][tid % kSeqWords] = 0u;
-  __syncthreads();
-  for (int r = 0; r < (two ? 2 : 1); ++r) {
-    const int t1 = row_ptr[row0 + r + 1];
-    for (int t = row_ptr[row0 + r] + tid; t < t1; t += blockDim.x) {
-      const int s = max(iv[2 * t], kb0) - kb0, e = min(iv[2 * t + 1], kb1) - kb0;
-      for (int q = s >> 5; s < e && q <= (e - 1) >> 5; ++q) {
-        const int lo = max(s - 32 * q, 0), hi = min(e - 32 * q, 32);
-        const uint32_t m = (hi == 32 ? ~0u : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
-        atomicOr(&L.bits[r][q], m);
-      }
-    }
-  }
-  __syncthreads();
   if (tid < 64) {
-    const uint32_t a = L.bits[0][tid], b = L.bits[1][tid], u = a | b;
+    const int word = kSeqWords * w + tid;
+    const uint32_t a = word < W ? bm0[word] : 0u;
+    const uint32_t b = two && word < W ? bm0[W + word] : 0u;
+    const uint32_t u = a | b;
     const int c = __builtin_popcount(u);
     int incl = c;   // inclusive prefix sum over the wave
 #pragma unroll
@@ -620,16 +608,17 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   bf16x8 pb[C::PS];
 
   __shared__ SeqLds sl;
-  const int row0 = mask_id * a.n_qb + qb0;
+  const int W = (a.n_kb + 31) >> 5;
+  const uint32_t* bm0 = a.bitmap + (int64_t(mask_id) * a.n_qb + qb0) * W;
   int seq_w = 0, seq_j = 1;
-  seq_build(sl, a.row_ptr, a.iv, row0, has_b, a.n_kb, 0);
+  seq_build(sl, bm0, has_b, W, 0);
   uint32_t seq_v = sl.seq[0];   // next entry, read one call ahead
   // Next block of the merged sequence; `mine` = my row keeps it.  All waves
   // call this at the same points, so a window refill may synchronize.
   auto pick = [&](int& kb, bool& mine) -> bool {
     uint32_t e = __builtin_amdgcn_readfirstlane(seq_v);
     if ((e & 0x3fffffffu) == kSeqRefill) {
-      seq_build(sl, a.row_ptr, a.iv, row0, has_b, a.n_kb, ++seq_w);
+      seq_build(sl, bm0, has_b, W, ++seq_w);
       e = __builtin_amdgcn_readfirstlane(sl.seq[0]);
       seq_j = 1;
     }
@@ -712,8 +701,19 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   // ---- epilogue ---------------------------------------------------------------
   const float l_tot = l_part + shfl_xor_f(l_part, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_row < N) {
-    __bf16* orow = O + int64_t(q_row) * D;
+  {
+    // lane indices recomputed here rather than kept live through the loop
+    int tid_e = threadIdx.x;
+    asm volatile("" : "+v"(tid_e));
+    const int wave = tid_e >> 6, lane = tid_e & 63, n = lane & 31, h = lane >> 5;
+    // O goes out through LDS (the tiles are free after the loop's last
+    // barrier): each wave writes its 32 x D block row-major into its own
+    // region (rows RS bytes apart), then stores whole rows, 16 bytes per
+    // lane, instead of 16-byte pieces of 32 rows per store.
+    constexpr int RS = D * 2 + 16, LPR = D * 2 / 16, RPI = 64 / LPR;
+    static_assert(2 * 32 * RS <= C::KBYTES && C::KBYTES == C::VBYTES, "staging fits the tiles");
+    char* stage = ((wave >> 1) == 0 ? kb_lds[0] : (wave >> 1) == 1 ? kb_lds[1]
+                   : (wave >> 1) == 2 ? vb_lds[0] : vb_lds[1]) + (wave & 1) * 32 * RS;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
@@ -721,9 +721,21 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
         bf16x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[dt][4 * g + j] * inv);
-        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * h) = w;
+        *reinterpret_cast<bf16x4*>(stage + n * RS + (dt * 32 + 8 * g + 4 * h) * 2) = w;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int qrow0 = (qb0 + grp) * C::BLK + w4 * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / LPR, c = lane % LPR;
+      const uint4 x = *reinterpret_cast<const uint4*>(stage + r * RS + c * 16);
+      if (qrow0 + r < N) *reinterpret_cast<uint4*>(O + int64_t(qrow0 + r) * D + c * 8) = x;
+    }
+  }
+  if (q_row < N) {
     if (a.lse && h == 0) {
       const float ln2 = 0.69314718055994530942f;
       a.lse[int64_t(bh) * N + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * ln2 : -INFINITY;

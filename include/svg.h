@@ -139,7 +139,7 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
 /* Softmax attention restricted, per query block, to the key blocks of the
  * head's mask row ([CalibAtt] sections 2.2 and 3.3; [VDA] section 2.1 for the
  * attention itself, section 5.3 for tiled online softmax).  Only the kept
- * blocks listed in the skip list are read.  Not causal.
+ * key blocks are read.  Not causal.
  *   q, k, v, o     : bf16 [B,H,N,D] frame-major.
  *   qp, kp, vp, op : bf16 [B,H,N,D] token-major twins; may be NULL when no
  *                    head uses layout 1.
@@ -158,8 +158,9 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  *                    aligned; may be NULL when the size is 0.  Its contents
  *                    need no initialisation and are overwritten by every call.
  * The masks' bitmap and skip list must describe the same mask (as
- * svg_encode_mask writes them): the kernel walks the skip list and uses the
- * bitmap to balance work.  A query block whose mask row is empty gets o = 0
+ * svg_encode_mask writes them): with 128-token blocks the kernel lists each
+ * pair of query blocks' kept key blocks from the bitmap (and balances work
+ * with it), with 64-token blocks it walks the skip list.  A query block whose mask row is empty gets o = 0
  * and lse = -inf.  bf16 inputs, fp32 accumulation and softmax, bf16 output
  * (P rounded to bf16 for the PV product; the softmax denominator sums the
  * fp32 weights). */
