@@ -516,8 +516,14 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
   l_part += l0 + l1;
 }
 
+// One work item: query blocks 2*pair and 2*pair+1 of head bh.  Every thread
+// of the workgroup calls it; it synchronizes.  In its last key-block
+// iteration thread 0 takes the index of its next item from the queue head
+// `qhead` into `next_idx`, so that the atomic's round trip overlaps the
+// item's last blocks.
 template <int D>
-__global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pairs, int pairs_per_xcd) {
+__device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, int32_t* qhead,
+                                          int& next_idx) {
   using C = Cfg2<D>;
   // Separate arrays per buffer, addressed with compile-time buffer indices:
   // the compiler can then tell that copies in flight target a buffer other
@@ -527,20 +533,9 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
   char* const kb_lds[2] = {reinterpret_cast<char*>(kbuf0), reinterpret_cast<char*>(kbuf1)};
   char* const vb_lds[2] = {reinterpret_cast<char*>(vbuf0), reinterpret_cast<char*>(vbuf1)};
 
-  // XCD-aware order: workgroup i runs on XCD i % 8 and takes item i / 8 of
-  // that XCD's work list (plan_kernel, order_kernel): the x-th of eight
-  // contiguous ranges of every head's query-block pairs, ranges of about equal
-  // work, heavy pairs first, otherwise head after head and pair after pair,
-  // so consecutive workgroups read the same key blocks through one L2.
-  const int xcd = blockIdx.x % 8;
-  const int local = blockIdx.x / 8;
-  const int32_t* counts = a.plan + a.BH * 9;
-  if (local >= counts[xcd]) return;
-  const int2 item = reinterpret_cast<const int2*>(a.plan + attn_plan_list_offset(a.BH))
-      [int64_t(xcd) * a.BH * pairs_per_xcd + local];
-  const int bh = item.x, pair = item.y;
-
-  const int tid = threadIdx.x;
+  // lane indices derived per item rather than kept live from one item to the next
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int wave = tid >> 6, lane = tid & 63;
   const int grp = wave >> 2;
   const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);   // wave within its group
@@ -652,6 +647,7 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
     int kb_next = 0;
     bool mine_next = false;
     const bool have_next = have_cur && pick(kb_next, mine_next);
+    if (have_cur && !have_next && tid == 0) next_idx = atomicAdd(qhead, 1);
 
     // ---- phase 1 --------------------------------------------------------------
     if (grp == 0) {
@@ -740,6 +736,50 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int pair
       const float ln2 = 0.69314718055994530942f;
       a.lse[int64_t(bh) * N + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * ln2 : -INFINITY;
     }
+  }
+}
+
+// Persistent workgroups, one per CU, take work items from eight queues, one
+// per XCD: workgroup i runs on XCD i % 8 and takes the items of that XCD's
+// work list (plan_kernel, order_kernel: the x-th of eight contiguous ranges
+// of every head's query-block pairs, ranges of about equal work, heavy pairs
+// first, otherwise head after head and pair after pair, so the XCD's CUs
+// read the same key blocks through one L2) in list order through an atomic
+// queue head.  A workgroup whose list is done takes items from the other
+// XCDs' lists.  Every item is computed the same way wherever it runs, so the
+// result does not depend on the schedule.
+template <int D>
+__global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap) {
+  const int xcd = blockIdx.x % 8;
+  const int32_t* counts = a.plan + a.BH * 9;
+  int32_t* heads = a.plan + a.BH * 9 + 8;
+  const int2* lists = reinterpret_cast<const int2*>(a.plan + attn_plan_list_offset(a.BH));
+  __shared__ int2 grabbed;
+  int next_idx = -1;   // thread 0: index in this XCD's queue taken ahead, -1 = none
+  auto take = [&]() -> int2 {
+    const int i = next_idx >= 0 ? next_idx : atomicAdd(heads + xcd, 1);
+    next_idx = -1;
+    if (i < counts[xcd]) return lists[int64_t(xcd) * cap + i];
+    for (int t = 1; t < 8; ++t) {
+      const int x = (xcd + t) & 7;
+      const int n = counts[x];
+      if (__hip_atomic_load(heads + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+      const int j = atomicAdd(heads + x, 1);
+      if (j < n) return lists[int64_t(x) * cap + j];
+    }
+    return make_int2(-1, 0);
+  };
+  for (;;) {
+    if (threadIdx.x == 0) grabbed = take();
+    __syncthreads();
+    const int bh = __builtin_amdgcn_readfirstlane(grabbed.x);
+    const int pair = __builtin_amdgcn_readfirstlane(grabbed.y);
+    if (bh < 0) break;
+    attn_pair<D>(a, bh, pair, heads + xcd, next_idx);
+    // attn_pair ends with no barrier: the next take must not overwrite
+    // `grabbed` before every wave has read it, nor the next item's copies
+    // land in tiles a slow wave still reads for its output
+    __syncthreads();
   }
 }
 
@@ -880,7 +920,10 @@ __global__ __launch_bounds__(256) void order_kernel(int n_kb, int BH, int pairs,
     else list[np++] = make_int2(h, p);
     ++i;
   });
-  if (tid == 0) counts[x] = total;
+  if (tid == 0) {
+    counts[x] = total;
+    counts[8 + x] = 0;   // queue head of the attention kernel
+  }
 }
 
 // V of every head, transposed per 128-key block into the workspace
@@ -918,6 +961,18 @@ void launch_t(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((attn_fwd_kernel<D, BLK>), grid, dim3(Cfg<D, BLK>::THREADS), 0, st, a);
 }
 
+// One workgroup per CU of the current device (the 128-block kernel's LDS
+// allows one per CU), a multiple of 8 so that every XCD gets as many, and no
+// more than there are items.
+int persistent_grid(int64_t items) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  const int64_t g = std::min<int64_t>(cus / 8 * 8, (items + 7) / 8 * 8);
+  return int(std::max<int64_t>(8, g));
+}
+
 template <int D>
 void launch_b128(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((vt_prep_kernel<D>), dim3(a.n_kb, a.BH), dim3(256), 0, st,
@@ -930,8 +985,8 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
                      a.n_qb, W, pairs, per_xcd, a.plan);
   hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.n_kb, a.BH, pairs, a.BH * per_xcd,
                      a.plan);
-  dim3 grid(8 * per_xcd * a.BH);
-  hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), grid, dim3(512), 0, st, a, pairs, per_xcd);
+  hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), dim3(persistent_grid(int64_t(a.BH) * pairs)),
+                     dim3(512), 0, st, a, a.BH * per_xcd);
 }
 
 }  // namespace

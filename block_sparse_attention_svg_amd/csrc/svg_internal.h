@@ -73,11 +73,12 @@ __host__ __device__ inline int plan_range_cap(int pairs) {
   return a > b ? a : b;
 }
 // Bytes of the work plan at the end of the attention workspace: 9 split
-// points per head, 8 list lengths, 8 work lists of (head, pair) int32 pairs,
+// points per head, 8 list lengths, 8 queue heads, 8 work lists of (head,
+// pair) int32 pairs,
 // each of capacity BH * plan_range_cap(pairs), then the work of every
 // (head, pair) as int32.
 // int32 offset of the work lists in the plan (8-byte aligned)
-__host__ __device__ inline size_t attn_plan_list_offset(int BH) { return (size_t(BH) * 9 + 8 + 1) & ~size_t(1); }
+__host__ __device__ inline size_t attn_plan_list_offset(int BH) { return (size_t(BH) * 9 + 16 + 1) & ~size_t(1); }
 // int32 offset of the per-pair work in the plan
 __host__ __device__ inline size_t attn_plan_work_offset(int BH, int pairs) {
   return attn_plan_list_offset(BH) + size_t(8) * BH * plan_range_cap(pairs) * 2;

@@ -154,9 +154,12 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  *   workspace      : device scratch of >= svg_attn_workspace_bytes(s) bytes
  *                    (V re-laid out per key block, then a plan that splits
  *                    every head's query-block pairs over the 8 XCDs into
- *                    ranges of equal work, from the mask bitmap); 16-byte
- *                    aligned; may be NULL when the size is 0.  Its contents
- *                    need no initialisation and are overwritten by every call.
+ *                    ranges of equal work, from the mask bitmap, and the
+ *                    heads of the 8 work queues the kernel's workgroups take
+ *                    those ranges from); 16-byte aligned; may be NULL when
+ *                    the size is 0.  Its contents need no initialisation and
+ *                    are overwritten by every call; calls in flight at the
+ *                    same time need separate workspaces.
  * The masks' bitmap and skip list must describe the same mask (as
  * svg_encode_mask writes them): with 128-token blocks the kernel lists each
  * pair of query blocks' kept key blocks from the bitmap (and balances work
@@ -173,7 +176,7 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
 
 /* Workspace bytes svg_block_sparse_attn needs for shape s (host function).
  * 128-token blocks: B*H*ceil(N/128)*128*D*2 (V transposed per key block), then
- * a work plan of (9*B*H + 8 rounded up to even)*4 + 8*B*H*cap*8 + B*H*pairs*4
+ * a work plan of (9*B*H + 16 rounded up to even)*4 + 8*B*H*cap*8 + B*H*pairs*4
  * bytes with pairs = ceil(ceil(N/128)/2) and cap = max(ceil(3*pairs/16),
  * ceil(pairs/8)).  64-token blocks: 0. */
 size_t svg_attn_workspace_bytes(svg_shape s);

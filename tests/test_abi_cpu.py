@@ -118,14 +118,14 @@ def test_attention_validation():
     a = list(base); a[10] = ctypes.byref(bad)
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
     # 128-token blocks: V^T blocks B*H*ceil(N/128)*128*D*2 bytes, then the work
-    # plan: (9*B*H + 8 int32, rounded to even) + 8 lists of B*H*cap int32 pairs
+    # plan: (9*B*H + 16 int32, rounded to even) + 8 lists of B*H*cap int32 pairs
     # + B*H*pairs int32, cap = max(ceil(3*pairs/16), ceil(pairs/8)),
     # pairs = ceil(ceil(N/128)/2)
     s128 = _shape(block=128)
     need = lib.svg_attn_workspace_bytes(s128)
     BH, pairs = 2, 4
     cap = max((3 * pairs + 15) // 16, (pairs + 7) // 8)
-    plan = ((9 * BH + 8 + 1) // 2 * 2) * 4 + 8 * BH * cap * 8 + BH * pairs * 4
+    plan = ((9 * BH + 16 + 1) // 2 * 2) * 4 + 8 * BH * cap * 8 + BH * pairs * 4
     assert need == 1 * 2 * 8 * 128 * 64 * 2 + plan
     assert lib.svg_attn_workspace_bytes(_shape()) == 0
     m128 = L.SvgMask(1, 8, 8, FAKE.value, FAKE.value, FAKE.value)
