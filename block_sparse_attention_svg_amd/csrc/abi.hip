@@ -207,6 +207,9 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
   size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
   if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
     return fail(SVG_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+  if (s.block == 128 && ((n_blocks(s) + 1) / 2 > 65535 || masks->n_masks > 32768))
+    return fail(SVG_ERR_UNSUPPORTED, "%s: 128-token blocks support up to 131070 blocks and 32768 masks",
+                fn);
   size_t need = attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SVG_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);

@@ -376,13 +376,21 @@ struct SeqLds {
   uint32_t seq[kSeqCap];
 };
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// (the Q rows of a new item) stay in flight across it.
+__device__ __forceinline__ void barrier_lds_only() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Builds window w from the bitmap rows bm0 (row 0) and bm0 + W (row 1, read
 // only when `two`); every thread of the workgroup calls it (it synchronizes).
 __device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict__ bm0, bool two,
                                           int W, int w) {
   const int tid = threadIdx.x;
   const int kb0 = 32 * kSeqWords * w;
-  __syncthreads();   // the previous window is no longer read
+  barrier_lds_only();   // the previous window is no longer read
   if (tid < 64) {
     const int word = kSeqWords * w + tid;
     const uint32_t a = word < W ? bm0[word] : 0u;
@@ -403,7 +411,7 @@ __device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict_
     const int total = __shfl(incl, 63, 64);
     if (tid == 0) L.seq[total] = (w + 1) * kSeqWords < W ? kSeqRefill : kSeqEnd;
   }
-  __syncthreads();
+  barrier_lds_only();
 }
 
 // S^T (128 keys x 32 queries) = K Q^T.  The scheduling barriers keep the K
@@ -516,14 +524,14 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
   l_part += l0 + l1;
 }
 
-// One work item: query blocks 2*pair and 2*pair+1 of head bh.  Every thread
-// of the workgroup calls it; it synchronizes.  In its last key-block
-// iteration thread 0 takes the index of its next item from the queue head
-// `qhead` into `next_idx`, so that the atomic's round trip overlaps the
-// item's last blocks.
+// One work item: query blocks 2*pair and 2*pair+1 of head bh, which uses
+// mask mask_id and, when tm, the token-major tensors.  Every thread of the
+// workgroup calls it; it synchronizes.  In its last key-block iteration
+// thread 0 takes the index of its next item from the queue head `qhead` into
+// `next_idx`, so that the atomic's round trip overlaps the item's last blocks.
 template <int D>
-__device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, int32_t* qhead,
-                                          int& next_idx) {
+__device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, int mask_id, bool tm,
+                                          int32_t* qhead, int& next_idx) {
   using C = Cfg2<D>;
   // Separate arrays per buffer, addressed with compile-time buffer indices:
   // the compiler can then tell that copies in flight target a buffer other
@@ -544,9 +552,6 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   const int qb0 = 2 * pair;
   const bool has_b = qb0 + 1 < a.n_qb;
 
-  int mask_id = a.head_mask ? a.head_mask[bh] : bh % a.n_masks;
-  mask_id = min(max(mask_id, 0), a.n_masks - 1);
-  const bool tm = a.head_layout && a.head_layout[bh] != 0;
   const int64_t head_off = int64_t(bh) * N * D;
   const __bf16* Q = static_cast<const __bf16*>(tm ? a.qp : a.q) + head_off;
   const char* Kh = reinterpret_cast<const char*>(static_cast<const __bf16*>(tm ? a.kp : a.k) + head_off);
@@ -767,15 +772,16 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap)
       const int j = atomicAdd(heads + x, 1);
       if (j < n) return lists[int64_t(x) * cap + j];
     }
-    return make_int2(-1, 0);
+    return make_int2(0, -1);   // every queue is empty
   };
   for (;;) {
     if (threadIdx.x == 0) grabbed = take();
     __syncthreads();
-    const int bh = __builtin_amdgcn_readfirstlane(grabbed.x);
-    const int pair = __builtin_amdgcn_readfirstlane(grabbed.y);
-    if (bh < 0) break;
-    attn_pair<D>(a, bh, pair, heads + xcd, next_idx);
+    // item: x = head | token-major flag << 31, y = pair | mask << 16 (order_kernel)
+    const int ix = __builtin_amdgcn_readfirstlane(grabbed.x);
+    const int iy = __builtin_amdgcn_readfirstlane(grabbed.y);
+    if (iy < 0) break;
+    attn_pair<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
     // attn_pair ends with no barrier: the next take must not overwrite
     // `grabbed` before every wave has read it, nor the next item's copies
     // land in tiles a slow wave still reads for its output
@@ -870,7 +876,9 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint32_t* __restrict__ 
 // stably partitioned so that heavy pairs (more than half of all key blocks in
 // the union of their two rows, e.g. the dense rows of text queries) come
 // first and start early.  One workgroup per XCD.
-__global__ __launch_bounds__(256) void order_kernel(int n_kb, int BH, int pairs, int cap,
+__global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ head_mask,
+                                                    const int32_t* __restrict__ head_layout, int n_masks,
+                                                    int n_kb, int BH, int pairs, int cap,
                                                     int32_t* __restrict__ plan) {
   const int x = blockIdx.x, tid = threadIdx.x;
   const int32_t* split = plan;
@@ -914,10 +922,18 @@ __global__ __launch_bounds__(256) void order_kernel(int n_kb, int BH, int pairs,
   int hp = hp0;                                   // next heavy slot
   int np = int(heavy_total) + (g0 - hp0);         // next normal slot
   i = 0;
+  // item (h, p) as x = h | token-major << 31, y = p | mask << 16, so that the
+  // attention kernel needs no further load to address its operands
+  auto entry = [&](int h, int p) {
+    int m = head_mask ? head_mask[h] : h % n_masks;
+    m = min(max(m, 0), n_masks - 1);
+    const bool tm = head_layout && head_layout[h] != 0;
+    return make_int2(h | (tm ? int(0x80000000u) : 0), p | (m << 16));
+  };
   walk([&](int h, int p) {
     const bool hv = i < 64 ? ((flags >> i) & 1) != 0 : heavy(h, p);
-    if (hv) list[hp++] = make_int2(h, p);
-    else list[np++] = make_int2(h, p);
+    if (hv) list[hp++] = entry(h, p);
+    else list[np++] = entry(h, p);
     ++i;
   });
   if (tid == 0) {
@@ -983,8 +999,8 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
   const int W = (a.n_kb + 31) / 32;
   hipLaunchKernelGGL(plan_kernel, dim3(a.BH), dim3(256), 0, st, a.bitmap, a.head_mask, a.n_masks,
                      a.n_qb, W, pairs, per_xcd, a.plan);
-  hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.n_kb, a.BH, pairs, a.BH * per_xcd,
-                     a.plan);
+  hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.head_mask, a.head_layout, a.n_masks,
+                     a.n_kb, a.BH, pairs, a.BH * per_xcd, a.plan);
   hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), dim3(persistent_grid(int64_t(a.BH) * pairs)),
                      dim3(512), 0, st, a, a.BH * per_xcd);
 }

@@ -143,7 +143,9 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  *   q, k, v, o     : bf16 [B,H,N,D] frame-major.
  *   qp, kp, vp, op : bf16 [B,H,N,D] token-major twins; may be NULL when no
  *                    head uses layout 1.
- *   masks          : host struct; n_qb == n_kb == ceil(N/block).
+ *   masks          : host struct; n_qb == n_kb == ceil(N/block); with
+ *                    128-token blocks at most 131070 blocks and 32768 masks
+ *                    (SVG_ERR_UNSUPPORTED beyond).
  *   head_mask      : device int32 [B*H]: mask index of each head (clamped to
  *                    [0, n_masks)); NULL means mask h % n_masks for head h.
  *   head_layout    : device int32 [B*H]: 0 = attend q,k,v -> o; nonzero =
