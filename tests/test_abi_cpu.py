@@ -117,6 +117,15 @@ def test_attention_validation():
     bad = _mask(n_masks=1, n=8)
     a = list(base); a[10] = ctypes.byref(bad)
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+    # 128-token blocks: work items hold the pair index in 16 bits and the mask
+    # index in 15, so longer rows or more masks are refused before any launch
+    big = _shape(block=128, N=128 * 131072)
+    a = list(base); a[3] = ctypes.c_void_p(1 << 40); a[8] = big
+    a[10] = ctypes.byref(_mask(n_masks=1, n=131072))
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_UNSUPPORTED
+    a = list(base); a[8] = _shape(block=128)
+    a[10] = ctypes.byref(_mask(n_masks=32769, n=8))
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_UNSUPPORTED
     # 128-token blocks: V^T blocks B*H*ceil(N/128)*128*D*2 bytes, then the work
     # plan: (9*B*H + 16 int32, rounded to even) + 8 lists of B*H*cap int32 pairs
     # + B*H*pairs int32, cap = max(ceil(3*pairs/16), ceil(pairs/8)),
