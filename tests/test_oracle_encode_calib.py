@@ -121,3 +121,74 @@ def test_static_workload_sparsity():
     assert abs(np.mean(kept) - 0.32) < 0.01
     M = O.calibrate_mask(S.energy_matrix(w, 0), w.eps)
     assert np.all(M.sum(axis=1) >= 1)          # eps > 0 never empties a row
+
+
+# ---- block energy, eps(t) schedule and the cross-prompt merge ([CalibAtt] section 3.1)
+
+def test_block_energy_rows_sum_to_query_counts():
+    # every query's softmax weights sum to 1, so row r of E sums to |r|;
+    # N = 300 with 64-blocks leaves a ragged last block of 44 queries
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((300, 32))
+    k = rng.standard_normal((300, 32))
+    E = O.block_energy(q, k, 0.3, 64)
+    assert E.shape == (5, 5)
+    np.testing.assert_allclose(E.sum(axis=1), [64, 64, 64, 64, 44], rtol=0, atol=1e-9)
+    assert (E > 0).all()
+
+
+def test_block_energy_uniform_attention():
+    # q = 0: every weight is 1/N, so E[r, c] = |r| |c| / N
+    N, B = 200, 64
+    rng = np.random.default_rng(12)
+    E = O.block_energy(np.zeros((N, 16)), rng.standard_normal((N, 16)), 1.0, B)
+    sizes = np.array([64, 64, 64, 8], dtype=np.float64)
+    np.testing.assert_allclose(E, np.outer(sizes, sizes) / N, rtol=1e-12)
+
+
+def test_block_energy_one_hot_attention_is_not_transposed():
+    # keys are orthonormal directions and query i points along key f(i), with a
+    # large scale: query i puts all its weight on key f(i), so E[r, c] counts
+    # the queries of block r whose partner lies in block c.  f is chosen so
+    # that this count matrix is not symmetric.
+    N, D, B = 48, 64, 16
+    rng = np.random.default_rng(13)
+    basis = np.linalg.qr(rng.standard_normal((D, D)))[0][:, :N].T   # N orthonormal rows
+    f = np.array([(3 * i + 17) % N if i < 16 else (i + 16) % N for i in range(N)])
+    E = O.block_energy(basis[f] * 40.0, basis, 1.0, B)
+    want = np.zeros((3, 3))
+    for i in range(N):
+        want[i // B, f[i] // B] += 1
+    assert not np.array_equal(want, want.T)
+    np.testing.assert_allclose(E, want, atol=1e-9)
+
+
+def test_block_energy_ignores_key_order_within_a_block():
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((128, 16))
+    k = rng.standard_normal((128, 16))
+    perm = np.concatenate([rng.permutation(32) + 32 * b for b in range(4)])
+    np.testing.assert_allclose(O.block_energy(q, k[perm], 0.5, 32), O.block_energy(q, k, 0.5, 32),
+                               rtol=1e-12)
+
+
+def test_eps_schedule_ends_midpoint_and_decay():
+    assert O.eps_schedule(0, 50) == 0.99
+    assert abs(O.eps_schedule(49, 50) - 0.84) < 1e-15
+    assert abs(O.eps_schedule(10, 21) - np.sqrt(0.99 * 0.84)) < 1e-15   # geometric midpoint
+    v = [O.eps_schedule(t, 50) for t in range(50)]
+    assert all(a > b for a, b in zip(v, v[1:]))
+    assert O.eps_schedule(0, 1) == 0.99
+
+
+def test_aggregate_masks_frequency_rule():
+    rng = np.random.default_rng(15)
+    M = (rng.random((4, 2, 6, 6)) < 0.5).astype(np.uint8)
+    np.testing.assert_array_equal(O.aggregate_masks(M[:1], 0.5), M[0])
+    np.testing.assert_array_equal(O.aggregate_masks(M, 1e-9), M.max(axis=0))     # union
+    np.testing.assert_array_equal(O.aggregate_masks(M, 1.0), M.min(axis=0))      # intersection
+    want = np.zeros_like(M[0])
+    for idx in itertools.product(*(range(n) for n in M.shape[1:])):
+        kept = sum(int(M[(p,) + idx]) for p in range(4))
+        want[idx] = 1 if 2 * kept >= 4 else 0                                    # rho = 0.5
+    np.testing.assert_array_equal(O.aggregate_masks(M, 0.5), want)
