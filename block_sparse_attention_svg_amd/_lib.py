@@ -48,6 +48,9 @@ _SIGS = {
     "svg_row_broadcast": (_I, [_P, SvgShape, _P, _I, _P]),
     "svg_restrict_anchor_rows": (_I, [_P, _I, SvgShape, _P, _I, _P]),
     "svg_calibrate_masks": (_I, [_P, _I, _I, _I, ctypes.c_double, _P, _P]),
+    "svg_block_energy": (_I, [_P, _P, SvgShape, ctypes.c_float, _P, _P]),
+    "svg_aggregate_masks": (_I, [_P, _I, ctypes.c_int64, ctypes.c_double, _P, _P]),
+    "svg_eps_schedule": (_I, [_I, _I, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
     "svg_status_string": (ctypes.c_char_p, [_I]),
     "svg_last_error": (ctypes.c_char_p, []),
     "svg_version": (ctypes.c_char_p, []),

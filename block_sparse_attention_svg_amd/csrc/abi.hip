@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <cmath>
+
 #include "svg_internal.h"
 
 namespace svg {
@@ -281,6 +283,40 @@ svg_status svg_calibrate_masks(const double* energy, int n_masks, int n_qb, int 
   if (!(eps > 0.0 && eps <= 1.0)) return fail(SVG_ERR_INVALID_ARG, "%s: eps must be in (0, 1]", fn);
   launch_calibrate(energy, n_masks, n_qb, n_kb, eps, out, as_stream(stream));
   return check_launch(fn);
+}
+
+svg_status svg_block_energy(const void* q, const void* k, svg_shape s, float scale, double* energy,
+                            void* stream) {
+  const char* fn = "svg_block_energy";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (!q || !k || !energy) return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / energy", fn);
+  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
+  if (int64_t(s.B) * s.H > 65535) return fail(SVG_ERR_UNSUPPORTED, "%s: more than 65535 heads", fn);
+  launch_block_energy(q, k, s, scale, energy, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_aggregate_masks(const uint8_t* masks, int n_sets, int64_t mask_elems, double rho,
+                               uint8_t* out, void* stream) {
+  const char* fn = "svg_aggregate_masks";
+  if (!masks || !out) return fail(SVG_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  if (n_sets < 1 || mask_elems < 1) return fail(SVG_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+  if (!(rho > 0.0 && rho <= 1.0)) return fail(SVG_ERR_INVALID_ARG, "%s: rho must be in (0, 1]", fn);
+  if (overlaps(out, masks, size_t(n_sets) * size_t(mask_elems)))
+    return fail(SVG_ERR_INVALID_ARG, "%s: out overlaps the candidate masks", fn);
+  launch_aggregate(masks, n_sets, mask_elems, rho, out, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_eps_schedule(int t, int T, double eps_first, double eps_last, double* eps) {
+  const char* fn = "svg_eps_schedule";
+  if (!eps) return fail(SVG_ERR_INVALID_ARG, "%s: NULL eps", fn);
+  if (T < 1 || t < 0 || t >= T) return fail(SVG_ERR_INVALID_ARG, "%s: need 0 <= t < T", fn);
+  if (!(eps_first > 0.0 && eps_first <= 1.0 && eps_last > 0.0 && eps_last <= 1.0))
+    return fail(SVG_ERR_INVALID_ARG, "%s: thresholds must be in (0, 1]", fn);
+  *eps = T == 1 ? eps_first : eps_first * std::pow(eps_last / eps_first, double(t) / double(T - 1));
+  return SVG_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,187 @@
+// Offline calibration on the GPU ([CalibAtt] section 3.1): the block
+// attention energy E(r, c) that the energy-threshold rule ranks, and the merge
+// of candidate masks over prompts by keep frequency.
+//
+// E(r, c) is the dense softmax weight the queries of block r give to the keys
+// of block c: sum over i in r, j in c of exp(s_ij - lse_i), s_ij = scale q_i.k_j.
+// One workgroup per (batch*head, query block), BLK/32 wavefronts of 32
+// queries.  Each key block is staged in LDS by the whole workgroup; S^T = K Q^T
+// runs on v_mfma_f32_32x32x16_bf16 with Q in registers (the attention kernel's
+// operand layout: lane l holds query l%32, dims 16*kk + 8*(l/32) + i).  The
+// first sweep over the key blocks keeps each query's running max and sum (log2
+// units); the second recomputes the scores, weighs them by exp2(s - lse) and
+// sums each block pair: per lane, then over the wave, then over the waves in
+// order, so the result is identical on every call.  fp32 arithmetic, float64
+// output for the threshold rule.
+#include "mfma_common.h"
+#include "svg_internal.h"
+
+namespace svg {
+namespace {
+
+template <int D, int BLK>
+struct ECfg {
+  static constexpr int NW = BLK / 32;          // wavefronts (32 queries each)
+  static constexpr int THREADS = NW * 64;
+  static constexpr int KT = BLK / 32;          // 32-key tiles per block
+  static constexpr int DK = D / 16;            // contraction steps
+  static constexpr int RS = D * 2 + 16;        // LDS row stride: 16 consecutive rows, distinct banks
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int LOADS = BLK * CPR / THREADS;
+  static_assert(BLK * CPR % THREADS == 0, "K staging divides evenly");
+};
+
+template <int D, int BLK>
+__device__ __forceinline__ void stage_k(char* ks, const __bf16* __restrict__ kh, int kb, int N, int tid) {
+  using C = ECfg<D, BLK>;
+#pragma unroll
+  for (int u = 0; u < C::LOADS; ++u) {
+    const int c = tid + u * C::THREADS;
+    const int row = c / C::CPR, col = c % C::CPR;
+    const int key = kb * BLK + row;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (key < N) x = *reinterpret_cast<const uint4*>(kh + int64_t(key) * D + col * 8);
+    *reinterpret_cast<uint4*>(ks + row * C::RS + col * 16) = x;
+  }
+}
+
+// S^T of one key block: sacc[kt] register r holds key kt*32 + 8*(r/4) +
+// 4*(lane/32) + r%4 of the block, query lane%32.
+template <int D, int BLK>
+__device__ __forceinline__ void scores(const char* ks, const bf16x8* qreg, int n, int h, f32x16* sacc) {
+  using C = ECfg<D, BLK>;
+#pragma unroll
+  for (int kt = 0; kt < C::KT; ++kt) {
+    sacc[kt] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) {
+      const uint4 a = *reinterpret_cast<const uint4*>(ks + (kt * 32 + n) * C::RS + (2 * kk + h) * 16);
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[kk], sacc[kt], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void energy_kernel(const __bf16* __restrict__ q,
+                                                         const __bf16* __restrict__ k, int N, int nB,
+                                                         float c2, double* __restrict__ E) {
+  using C = ECfg<D, BLK>;
+  __shared__ __attribute__((aligned(16))) char ks[BLK * C::RS];
+  __shared__ float part[C::NW];
+  const int r = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const __bf16* qh = q + int64_t(bh) * N * D;
+  const __bf16* kh = k + int64_t(bh) * N * D;
+  const int qi = r * BLK + wave * 32 + n;
+  const bool q_ok = qi < N;
+  bf16x8 qreg[C::DK];
+#pragma unroll
+  for (int kk = 0; kk < C::DK; ++kk) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (q_ok) u = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * kk + 8 * h);
+    qreg[kk] = as_bf16x8(u);
+  }
+  f32x16 sacc[C::KT];
+  auto key_of = [&](int kb, int kt, int i) { return kb * BLK + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3); };
+
+  // sweep 1: running max m and this lane's share l of the sum (log2 units)
+  float m = -INFINITY, l = 0.f;
+  for (int kb = 0; kb < nB; ++kb) {
+    __syncthreads();   // the previous block's tile is no longer read
+    stage_k<D, BLK>(ks, kh, kb, N, tid);
+    __syncthreads();
+    scores<D, BLK>(ks, qreg, n, h, sacc);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (key_of(kb, kt, i) >= N) sacc[kt][i] = -INFINITY;
+        mx = fmaxf(mx, sacc[kt][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    const float m_new = fmaxf(m, mx);
+    float add = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) add += fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -m_new));
+    l = l * fast_exp2(m - m_new) + add;
+    m = m_new;
+  }
+  const float lse2 = m + __log2f(l + __shfl_xor(l, 32, 64));
+
+  // sweep 2: block sums of exp2(s - lse)
+  double* row = E + (int64_t(bh) * nB + r) * nB;
+  for (int kb = 0; kb < nB; ++kb) {
+    __syncthreads();
+    stage_k<D, BLK>(ks, kh, kb, N, tid);
+    __syncthreads();
+    scores<D, BLK>(ks, qreg, n, h, sacc);
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+        sum += key_of(kb, kt, i) < N ? p : 0.f;
+      }
+    if (!q_ok) sum = 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) part[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) t += part[w];
+      row[kb] = double(t);
+    }
+  }
+}
+
+// out[e] = 1 when the fraction of the n_sets candidate masks that keep
+// element e reaches rho, the fraction taken in float64.
+__global__ __launch_bounds__(256) void aggregate_kernel(const uint8_t* __restrict__ masks, int n_sets,
+                                                        int64_t elems, double rho,
+                                                        uint8_t* __restrict__ out) {
+  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < elems;
+       e += int64_t(gridDim.x) * blockDim.x) {
+    int count = 0;
+    for (int p = 0; p < n_sets; ++p) count += masks[int64_t(p) * elems + e] != 0;
+    out[e] = double(count) / double(n_sets) >= rho ? 1 : 0;
+  }
+}
+
+template <int D, int BLK>
+void launch_energy_t(const __bf16* q, const __bf16* k, const svg_shape& s, float scale, double* E,
+                     hipStream_t st) {
+  const int nB = ceil_div(s.N, BLK);
+  hipLaunchKernelGGL((energy_kernel<D, BLK>), dim3(nB, s.B * s.H), dim3(BLK * 2), 0, st, q, k, s.N, nB,
+                     scale * 1.4426950408889634f, E);
+}
+
+}  // namespace
+
+void launch_block_energy(const void* q, const void* k, const svg_shape& s, float scale, double* E,
+                         hipStream_t st) {
+  const __bf16* qb = static_cast<const __bf16*>(q);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  if (s.block == 128) {
+    if (s.D == 128) launch_energy_t<128, 128>(qb, kb, s, scale, E, st);
+    else launch_energy_t<64, 128>(qb, kb, s, scale, E, st);
+  } else {
+    if (s.D == 128) launch_energy_t<128, 64>(qb, kb, s, scale, E, st);
+    else launch_energy_t<64, 64>(qb, kb, s, scale, E, st);
+  }
+}
+
+void launch_aggregate(const uint8_t* masks, int n_sets, int64_t elems, double rho, uint8_t* out,
+                      hipStream_t st) {
+  const int64_t blocks = std::min<int64_t>((elems + 255) / 256, 65535);
+  hipLaunchKernelGGL(aggregate_kernel, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, st,
+                     masks, n_sets, elems, rho, out);
+}
+
+}  // namespace svg

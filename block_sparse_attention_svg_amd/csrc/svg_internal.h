@@ -38,6 +38,10 @@ struct FastDiv {
 void launch_build_masks(const svg_shape& s, int band_w, uint8_t* masks, hipStream_t st);
 void launch_restrict_anchor_rows(uint8_t* masks, int n_masks, const svg_shape& s,
                                  const int32_t* mask_sel, int k, hipStream_t st);
+void launch_block_energy(const void* q, const void* k, const svg_shape& s, float scale, double* E,
+                         hipStream_t st);
+void launch_aggregate(const uint8_t* masks, int n_sets, int64_t elems, double rho, uint8_t* out,
+                      hipStream_t st);
 void launch_calibrate(const double* E, int n_masks, int n_qb, int n_kb, double eps,
                       uint8_t* out, hipStream_t st);
 void launch_encode(const uint8_t* dense, int n_masks, int n_qb, int n_kb, uint32_t* bitmap,

@@ -219,5 +219,43 @@ def svg_calibrate_masks(energy: torch.Tensor, eps: float, out: torch.Tensor = No
     return out
 
 
+def svg_block_energy(q: torch.Tensor, k: torch.Tensor, s: Shape, scale: float,
+                     out: torch.Tensor = None) -> torch.Tensor:
+    """float64 [B*H, nB, nB] block attention energies of every head."""
+    _need_act(q, "q", s)
+    _need_act(k, "k", s)
+    nB = s.n_blocks
+    if out is None:
+        out = torch.empty((s.B * s.H, nB, nB), dtype=torch.float64, device=q.device)
+    _need(out, "out", torch.float64)
+    if tuple(out.shape) != (s.B * s.H, nB, nB):
+        raise ValueError(f"out must be [{s.B * s.H}, {nB}, {nB}]")
+    L.check("svg_block_energy", L.lib().svg_block_energy(_ptr(q), _ptr(k), s.c(), float(scale),
+                                                         _ptr(out), _stream()))
+    return out
+
+
+def svg_aggregate_masks(masks: torch.Tensor, rho: float = 0.5, out: torch.Tensor = None) -> torch.Tensor:
+    """uint8 mask of the elements kept by at least a fraction rho of the
+    candidate masks stacked along dim 0."""
+    _need(masks, "masks", torch.uint8)
+    if out is None:
+        out = torch.empty(masks.shape[1:], dtype=torch.uint8, device=masks.device)
+    _need(out, "out", torch.uint8)
+    if tuple(out.shape) != tuple(masks.shape[1:]):
+        raise ValueError("out must have the shape of one candidate mask")
+    L.check("svg_aggregate_masks", L.lib().svg_aggregate_masks(
+        _ptr(masks), masks.shape[0], out.numel(), float(rho), _ptr(out), _stream()))
+    return out
+
+
+def svg_eps_schedule(t: int, T: int, eps_first: float = 0.99, eps_last: float = 0.84) -> float:
+    """Energy threshold of denoising step t of T (host)."""
+    v = ctypes.c_double()
+    L.check("svg_eps_schedule", L.lib().svg_eps_schedule(int(t), int(T), float(eps_first),
+                                                         float(eps_last), ctypes.byref(v)))
+    return v.value
+
+
 def svg_version() -> str:
     return L.lib().svg_version().decode()

@@ -183,6 +183,36 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
  * ceil(pairs/8)).  64-token blocks: 0. */
 size_t svg_attn_workspace_bytes(svg_shape s);
 
+/* ---- offline calibration ([CalibAtt] section 3.1) --------------------------- */
+/* Block attention energy: energy[bh][r][c] = sum over the queries i of block r
+ * and the keys j of block c of the dense softmax weight exp(s_ij - lse_i),
+ * s_ij = scale * q_i.k_j, lse_i over all N keys: the E(r, c) that the
+ * energy-threshold rule (svg_calibrate_masks) ranks.  Each row sums to the
+ * number of queries in block r.
+ *   q, k   : bf16 [B,H,N,D], blocks taken in this layout (block = s.block).
+ *   energy : device double [B*H, nB, nB] out, nB = ceil(N/block).
+ * Two sweeps over the keys per query block (running max and sum, then block
+ * sums); fp32 arithmetic, sums in a fixed order (identical on every call).
+ * Errors: SVG_ERR_INVALID_ARG for NULL pointers or scale <= 0,
+ * SVG_ERR_UNSUPPORTED for D or block outside {64, 128} or B*H > 65535. */
+svg_status svg_block_energy(const void* q, const void* k, svg_shape s, float scale, double* energy,
+                            void* stream);
+
+/* Merge of candidate masks over prompts: out[e] = 1 when the fraction of the
+ * n_sets masks that keep element e reaches rho (count / n_sets >= rho in
+ * double), else 0.
+ *   masks : device uint8 [n_sets][mask_elems] (nonzero = kept); out: device
+ *           uint8 [mask_elems], not overlapping masks.  0 < rho <= 1. */
+svg_status svg_aggregate_masks(const uint8_t* masks, int n_sets, int64_t mask_elems, double rho,
+                               uint8_t* out, void* stream);
+
+/* Energy threshold of denoising step t of T (host function): an exponential
+ * decay from eps_first at t = 0 to eps_last at t = T-1,
+ * eps_first * (eps_last / eps_first)^(t / (T-1)); eps_first when T == 1.
+ * The pages give about 0.99 early and 0.84 late.  Needs 0 <= t < T and both
+ * thresholds in (0, 1]. */
+svg_status svg_eps_schedule(int t, int T, double eps_first, double eps_last, double* eps);
+
 /* ---- a7: row-repetitive heads ------------------------------------------- */
 /* Anchor-row broadcast ([CalibAtt] section 3.2): in every frame, latent row y
  * takes the output of its anchor row a(y) = floor((2j+1)*Hs/(2k)) with
