@@ -245,6 +245,21 @@ def main():
         kv_bytes = 2 * w.B * w.H * tensor_bytes
         out["profile_gbs"] = round(kv_bytes / (per["profile"] * 1e-3) / 1e9, 1)
         out["profile_share"] = round(per["profile"] / ms_step, 4)
+    if w.mode == "static":
+        # offline calibration's block-energy pass over every head, timed once
+        # after a warm-up call (not part of the layer step)
+        e_out = svg.svg_block_energy(q, k, s, scale)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        svg.svg_block_energy(q, k, s, scale, out=e_out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        e_ms = e0.elapsed_time(e1)
+        e_flop = 2.0 * w.B * w.H * w.N * w.N * w.D            # one Q K^T per head
+        out["calibration_energy"] = {"ms": round(e_ms, 3), "tflops": round(e_flop / (e_ms * 1e-3) / 1e12, 2),
+                                     "note": "block attention energies of all heads; FLOP = one QK^T "
+                                             "(the kernel computes it twice: max/sum, then block sums)"}
+        del e_out
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, classes, args.cpu_seconds)
     else:
