@@ -31,17 +31,27 @@ struct ECfg {
   static_assert(BLK * CPR % THREADS == 0, "K staging divides evenly");
 };
 
+// K block kb into registers (rows past N as zero), then into an LDS tile:
+// the loads of block kb+1 are in flight while block kb is computed.
 template <int D, int BLK>
-__device__ __forceinline__ void stage_k(char* ks, const __bf16* __restrict__ kh, int kb, int N, int tid) {
+__device__ __forceinline__ void load_k(uint4* kr, const __bf16* __restrict__ kh, int kb, int N, int tid) {
   using C = ECfg<D, BLK>;
 #pragma unroll
   for (int u = 0; u < C::LOADS; ++u) {
     const int c = tid + u * C::THREADS;
     const int row = c / C::CPR, col = c % C::CPR;
     const int key = kb * BLK + row;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (key < N) x = *reinterpret_cast<const uint4*>(kh + int64_t(key) * D + col * 8);
-    *reinterpret_cast<uint4*>(ks + row * C::RS + col * 16) = x;
+    kr[u] = key < N ? *reinterpret_cast<const uint4*>(kh + int64_t(key) * D + col * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void store_k(char* ks, const uint4* kr, int tid) {
+  using C = ECfg<D, BLK>;
+#pragma unroll
+  for (int u = 0; u < C::LOADS; ++u) {
+    const int c = tid + u * C::THREADS;
+    *reinterpret_cast<uint4*>(ks + (c / C::CPR) * C::RS + (c % C::CPR) * 16) = kr[u];
   }
 }
 
@@ -62,12 +72,14 @@ __device__ __forceinline__ void scores(const char* ks, const bf16x8* qreg, int n
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void energy_kernel(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(BLK * 2, 2) void energy_kernel(const __bf16* __restrict__ q,
                                                          const __bf16* __restrict__ k, int N, int nB,
                                                          float c2, double* __restrict__ E) {
   using C = ECfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) char ks[BLK * C::RS];
-  __shared__ float part[C::NW];
+  // two K tiles: block kb in tile kb % 2, so one barrier per block orders both
+  // the tile refill and the per-wave block sums
+  __shared__ __attribute__((aligned(16))) char ks[2][BLK * C::RS];
+  __shared__ float part[2][C::NW];
   const int r = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, h = lane >> 5;
@@ -85,13 +97,16 @@ __global__ __launch_bounds__(BLK * 2) void energy_kernel(const __bf16* __restric
   f32x16 sacc[C::KT];
   auto key_of = [&](int kb, int kt, int i) { return kb * BLK + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3); };
 
+  uint4 kr[C::LOADS];
   // sweep 1: running max m and this lane's share l of the sum (log2 units)
   float m = -INFINITY, l = 0.f;
+  load_k<D, BLK>(kr, kh, 0, N, tid);
   for (int kb = 0; kb < nB; ++kb) {
-    __syncthreads();   // the previous block's tile is no longer read
-    stage_k<D, BLK>(ks, kh, kb, N, tid);
+    char* tile = ks[kb & 1];
+    store_k<D, BLK>(tile, kr, tid);   // tile kb%2 was last read for block kb-2
     __syncthreads();
-    scores<D, BLK>(ks, qreg, n, h, sacc);
+    if (kb + 1 < nB) load_k<D, BLK>(kr, kh, kb + 1, N, tid);
+    scores<D, BLK>(tile, qreg, n, h, sacc);
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt)
@@ -112,13 +127,24 @@ __global__ __launch_bounds__(BLK * 2) void energy_kernel(const __bf16* __restric
   }
   const float lse2 = m + __log2f(l + __shfl_xor(l, 32, 64));
 
-  // sweep 2: block sums of exp2(s - lse)
+  // sweep 2: block sums of exp2(s - lse); block kb's per-wave sums are added
+  // up (in wave order) after the next barrier
   double* row = E + (int64_t(bh) * nB + r) * nB;
+  auto finish = [&](int kb) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) t += part[kb & 1][w];
+    row[kb] = double(t);
+  };
+  __syncthreads();   // every wave is done with sweep 1's tiles
+  load_k<D, BLK>(kr, kh, 0, N, tid);
   for (int kb = 0; kb < nB; ++kb) {
+    char* tile = ks[kb & 1];
+    store_k<D, BLK>(tile, kr, tid);
     __syncthreads();
-    stage_k<D, BLK>(ks, kh, kb, N, tid);
-    __syncthreads();
-    scores<D, BLK>(ks, qreg, n, h, sacc);
+    if (kb > 0 && tid == 0) finish(kb - 1);
+    if (kb + 1 < nB) load_k<D, BLK>(kr, kh, kb + 1, N, tid);
+    scores<D, BLK>(tile, qreg, n, h, sacc);
     float sum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt)
@@ -130,15 +156,10 @@ __global__ __launch_bounds__(BLK * 2) void energy_kernel(const __bf16* __restric
     if (!q_ok) sum = 0.f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if (lane == 0) part[wave] = sum;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < C::NW; ++w) t += part[w];
-      row[kb] = double(t);
-    }
+    if (lane == 0) part[kb & 1][wave] = sum;   // read after the next barrier
   }
+  __syncthreads();
+  if (tid == 0) finish(nB - 1);
 }
 
 // out[e] = 1 when the fraction of the n_sets candidate masks that keep
