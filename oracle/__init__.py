@@ -23,7 +23,7 @@ from .attention import dense_attention, block_masked_attention, head_attention
 from .encode import encode_masks, decode_masks, iv_capacity
 from .profiler import profile_heads, profile_errors_decomposed
 from .calibrate import calibrate_row, calibrate_mask, block_energy, eps_schedule, aggregate_masks
-from .broadcast import row_broadcast
+from .broadcast import row_broadcast, row_patterns, row_similarity, is_row_repetitive
 from .flops import kept_pairs, algorithmic_flops
 
 __all__ = [
@@ -33,6 +33,6 @@ __all__ = [
     "dense_attention", "block_masked_attention", "head_attention",
     "encode_masks", "decode_masks", "iv_capacity",
     "profile_heads", "profile_errors_decomposed",
-    "calibrate_row", "calibrate_mask", "block_energy", "eps_schedule", "aggregate_masks", "row_broadcast",
+    "calibrate_row", "calibrate_mask", "block_energy", "eps_schedule", "aggregate_masks", "row_broadcast", "row_patterns", "row_similarity", "is_row_repetitive",
     "kept_pairs", "algorithmic_flops",
 ]

@@ -144,3 +144,41 @@ def test_row_broadcast():
                 assert np.array_equal(b[row], o[row])
     assert np.array_equal(b[F * Hs * Ws:], o[F * Hs * Ws:])
     assert np.array_equal(O.row_broadcast(o, F, Hs, Ws, Hs), o)
+
+
+# ---- row-repetitive head test: mean cosine of the rows' attention patterns
+
+def test_row_similarity_uniform_attention_is_one():
+    # q = 0: every query spreads its weight evenly, so all rows share one pattern
+    F, Hs, Ws = 2, 4, 8
+    N = F * Hs * Ws + 5                                   # a text tail as well
+    rng = np.random.default_rng(31)
+    A = O.row_patterns(np.zeros((N, 16)), rng.standard_normal((N, 16)), 1.0, F, Hs, Ws)
+    np.testing.assert_allclose(A, Ws / N, rtol=1e-12)
+    assert abs(O.row_similarity(np.zeros((N, 16)), rng.standard_normal((N, 16)), 1.0, F, Hs, Ws) - 1) < 1e-12
+    assert O.is_row_repetitive(1.0) and not O.is_row_repetitive(0.87)
+
+
+def test_row_similarity_rows_attending_their_own_row_is_zero():
+    # keys of each latent row point along their own orthonormal direction and
+    # the queries of a row along their row's direction, with a large scale:
+    # row patterns sit on disjoint key sets, every cosine is 0
+    F, Hs, Ws, D = 2, 3, 4, 8
+    N = F * Hs * Ws
+    rng = np.random.default_rng(32)
+    U = np.linalg.qr(rng.standard_normal((D, D)))[0][:, :F * Hs].T
+    rows = np.repeat(np.arange(F * Hs), Ws)
+    assert O.row_similarity(U[rows] * 60.0, U[rows], 1.0, F, Hs, Ws) < 1e-12
+
+
+def test_row_similarity_two_groups_closed_form():
+    # rows y < Hs/2 attend (evenly) to key set A, the others to key set B,
+    # disjoint: a pair in one group has cosine 1, a mixed pair 0, so the mean
+    # is 2 C(Hs/2, 2) / C(Hs, 2) = 1/3 for Hs = 4
+    F, Hs, Ws, D = 3, 4, 5, 8
+    N = F * Hs * Ws
+    e = np.eye(D)
+    y = (np.arange(N) // Ws) % Hs
+    q = np.where((y < Hs // 2)[:, None], e[0], e[1]) * 50.0
+    k = np.where((y < Hs // 2)[:, None], e[0], e[1])
+    assert abs(O.row_similarity(q, k, 1.0, F, Hs, Ws) - 1.0 / 3.0) < 1e-12
