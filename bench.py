@@ -260,6 +260,20 @@ def main():
                                      "note": "block attention energies of all heads; FLOP = one QK^T "
                                              "(the kernel computes it twice: max/sum, then block sums)"}
         del e_out
+        # and the row-repetitive head test over every head (row patterns + Gram)
+        r_ws = torch.empty(svg.svg_row_similarity_workspace_bytes(s), dtype=torch.uint8, device=dev)
+        svg.svg_row_similarity(q, k, s, scale, workspace=r_ws)
+        e0.record(stream)
+        r_score = svg.svg_row_similarity(q, k, s, scale, workspace=r_ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        r_ms = e0.elapsed_time(e1)
+        out["calibration_rows"] = {"ms": round(r_ms, 3),
+                                   "tflops": round(e_flop / (r_ms * 1e-3) / 1e12, 2),
+                                   "repetitive_heads": int((r_score > 0.87).sum().item()),
+                                   "note": "row attention patterns of all heads + per-frame cosines; "
+                                           "FLOP = one QK^T (computed twice)"}
+        del r_ws
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, classes, args.cpu_seconds)
     else:

@@ -10,7 +10,8 @@ from .ops import (
     svg_build_masks, svg_encode_iv_capacity, svg_encode_mask, svg_permute,
     svg_profile_workspace_bytes, svg_profile_heads, svg_attn_workspace_bytes,
     svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows, svg_calibrate_masks, svg_version,
-    svg_block_energy, svg_aggregate_masks, svg_eps_schedule,
+    svg_block_energy, svg_aggregate_masks, svg_eps_schedule, svg_row_similarity,
+    svg_row_similarity_workspace_bytes,
 )
 from .layer import OnlineSparseAttention, StaticSparseAttention, attention_flops, kept_pairs_per_mask
 from ._lib import SvgError, LIB_PATH
@@ -20,7 +21,8 @@ __all__ = [
     "svg_permute", "svg_profile_workspace_bytes", "svg_profile_heads", "svg_attn_workspace_bytes",
     "svg_block_sparse_attn",
     "svg_row_broadcast", "svg_restrict_anchor_rows", "svg_calibrate_masks", "svg_version",
-    "svg_block_energy", "svg_aggregate_masks", "svg_eps_schedule",
+    "svg_block_energy", "svg_aggregate_masks", "svg_eps_schedule", "svg_row_similarity",
+    "svg_row_similarity_workspace_bytes",
     "OnlineSparseAttention", "StaticSparseAttention", "attention_flops", "kept_pairs_per_mask",
     "SvgError", "LIB_PATH",
 ]

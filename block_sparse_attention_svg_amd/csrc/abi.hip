@@ -309,6 +309,30 @@ svg_status svg_aggregate_masks(const uint8_t* masks, int n_sets, int64_t mask_el
   return check_launch(fn);
 }
 
+size_t svg_row_similarity_workspace_bytes(svg_shape s) {
+  if (check_shape(s, "svg_row_similarity_workspace_bytes") != SVG_OK) return 0;
+  return row_similarity_workspace_bytes(s);
+}
+
+svg_status svg_row_similarity(const void* q, const void* k, svg_shape s, float scale, double* score,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "svg_row_similarity";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (!q || !k || !score) return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / score", fn);
+  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
+  if (s.Ws > 128 || s.Hs < 2 || s.Hs > 64)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: needs Ws <= 128 and 2 <= Hs <= 64", fn);
+  if (int64_t(s.B) * s.H > 65535) return fail(SVG_ERR_UNSUPPORTED, "%s: more than 65535 heads", fn);
+  const size_t need = row_similarity_workspace_bytes(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(SVG_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(SVG_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  launch_row_similarity(q, k, s, scale, score, workspace, as_stream(stream));
+  return check_launch(fn);
+}
+
 svg_status svg_eps_schedule(int t, int T, double eps_first, double eps_last, double* eps) {
   const char* fn = "svg_eps_schedule";
   if (!eps) return fail(SVG_ERR_INVALID_ARG, "%s: NULL eps", fn);

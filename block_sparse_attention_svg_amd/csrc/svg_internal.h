@@ -42,6 +42,9 @@ void launch_block_energy(const void* q, const void* k, const svg_shape& s, float
                          hipStream_t st);
 void launch_aggregate(const uint8_t* masks, int n_sets, int64_t elems, double rho, uint8_t* out,
                       hipStream_t st);
+size_t row_similarity_workspace_bytes(const svg_shape& s);
+void launch_row_similarity(const void* q, const void* k, const svg_shape& s, float scale, double* score,
+                           void* ws, hipStream_t st);
 void launch_calibrate(const double* E, int n_masks, int n_qb, int n_kb, double eps,
                       uint8_t* out, hipStream_t st);
 void launch_encode(const uint8_t* dense, int n_masks, int n_qb, int n_kb, uint32_t* bitmap,

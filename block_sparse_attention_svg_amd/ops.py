@@ -249,6 +249,25 @@ def svg_aggregate_masks(masks: torch.Tensor, rho: float = 0.5, out: torch.Tensor
     return out
 
 
+def svg_row_similarity_workspace_bytes(s: Shape) -> int:
+    return int(L.lib().svg_row_similarity_workspace_bytes(s.c()))
+
+
+def svg_row_similarity(q: torch.Tensor, k: torch.Tensor, s: Shape, scale: float,
+                       workspace: torch.Tensor = None) -> torch.Tensor:
+    """float64 [B*H] mean within-frame cosine of the rows' attention patterns."""
+    _need_act(q, "q", s)
+    _need_act(k, "k", s)
+    need = svg_row_similarity_workspace_bytes(s)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    out = torch.empty(s.B * s.H, dtype=torch.float64, device=q.device)
+    L.check("svg_row_similarity", L.lib().svg_row_similarity(
+        _ptr(q), _ptr(k), s.c(), float(scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
 def svg_eps_schedule(t: int, T: int, eps_first: float = 0.99, eps_last: float = 0.84) -> float:
     """Energy threshold of denoising step t of T (host)."""
     v = ctypes.c_double()

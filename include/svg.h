@@ -206,6 +206,24 @@ svg_status svg_block_energy(const void* q, const void* k, svg_shape s, float sca
 svg_status svg_aggregate_masks(const uint8_t* masks, int n_sets, int64_t mask_elems, double rho,
                                uint8_t* out, void* stream);
 
+/* Row-repetitive head test ([CalibAtt] section 3.2): for every head, the mean
+ * over frames and over pairs of distinct latent rows of a frame of the cosine
+ * similarity of the two rows' attention patterns, a row's pattern being the
+ * sum of the dense softmax weights of its Ws queries over all N keys.  A head
+ * whose score exceeds gamma (0.87 on the pages) is row-repetitive
+ * (svg_restrict_anchor_rows, svg_row_broadcast).
+ *   q, k      : bf16 [B,H,N,D] frame-major (rows are Ws consecutive tokens).
+ *   score     : device double [B*H] out.
+ *   workspace : device, >= svg_row_similarity_workspace_bytes(s) bytes,
+ *               256-byte aligned: the row patterns, float [B*H][F*Hs][N],
+ *               then per-frame sums (Wan 720p: 286 MB per head).
+ * fp32 weights and pattern sums, float64 Gram sums, fixed order (identical on
+ * every call).  SVG_ERR_UNSUPPORTED for Ws > 128, Hs outside [2, 64], D
+ * outside {64, 128} or B*H > 65535; SVG_ERR_CAPACITY for a short workspace. */
+size_t svg_row_similarity_workspace_bytes(svg_shape s);
+svg_status svg_row_similarity(const void* q, const void* k, svg_shape s, float scale, double* score,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Energy threshold of denoising step t of T (host function): an exponential
  * decay from eps_first at t = 0 to eps_last at t = T-1,
  * eps_first * (eps_last / eps_first)^(t / (T-1)); eps_first when T == 1.

@@ -169,3 +169,29 @@ def test_flop_count_from_skip_list():
     m = svg.EncodedMasks(2, 3, 3, torch.zeros(1), rp, iv)
     pairs = kept_pairs_per_mask(m, N, B)
     assert pairs.tolist() == [64 * 64 + 22 * 22, N * N]
+
+
+def test_calibration_validation():
+    lib = L.lib()
+    s = _shape()
+    m = ctypes.c_void_p(0x30000000)
+    assert lib.svg_block_energy(None, FAKE, s, 0.1, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_block_energy(FAKE, FAKE, s, 0.0, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_block_energy(FAKE, FAKE, _shape(D=80), 0.1, FAKE2, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_aggregate_masks(FAKE, 0, 10, 0.5, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_aggregate_masks(FAKE, 2, 10, 0.0, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_aggregate_masks(FAKE, 2, 10, 1.5, FAKE2, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_aggregate_masks(FAKE, 2, 10, 0.5, ctypes.c_void_p(FAKE.value + 5), None) == L.SVG_ERR_INVALID_ARG
+    v = ctypes.c_double()
+    assert lib.svg_eps_schedule(3, 3, 0.99, 0.84, ctypes.byref(v)) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_eps_schedule(0, 1, 0.99, 1.5, ctypes.byref(v)) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_eps_schedule(2, 5, 0.99, 0.84, ctypes.byref(v)) == L.SVG_OK
+    assert abs(v.value - (0.99 * 0.84) ** 0.5) < 1e-15
+    ws = lib.svg_row_similarity_workspace_bytes(s)
+    assert ws >= 1 * 2 * 4 * 16 * 1024 * 4
+    big = ctypes.c_void_p(1 << 40)
+    assert lib.svg_row_similarity(FAKE, FAKE, s, 0.1, FAKE2, big, ws - 1, None) == L.SVG_ERR_CAPACITY
+    assert lib.svg_row_similarity(FAKE, FAKE, s, 0.1, FAKE2, ctypes.c_void_p((1 << 40) + 16), ws, None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_row_similarity(FAKE, FAKE, _shape(Ws=256, N=4 * 16 * 256), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=1, Ws=256, N=1024), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=65, Ws=4, N=1040), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED

@@ -158,3 +158,100 @@ def test_calibration_chain_from_gpu_energies():
     np.testing.assert_array_equal(merged, O.aggregate_masks(want_c, 0.5))
     # a merged mask keeps every row's most energetic block of the majority of prompts
     assert merged.sum() > 0
+
+
+# ---- row-repetitive head test ([CalibAtt] section 3.2) ------------------------
+
+def _pattern_bound(q, k, scale, Ws, rows):
+    """Oracle row patterns of `rows` and the largest relative error an entry may
+    carry: each weight's fp32 error (as in energy_bound) plus a 128-term sum."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    N, D = q.shape
+    c2 = scale / math.log(2.0)
+    kn = np.linalg.norm(k, axis=1)
+    A = np.zeros((len(rows), N))
+    worst = 0.0
+    for a, r in enumerate(rows):
+        qi = q[r * Ws:(r + 1) * Ws]
+        s = (qi @ k.T) * scale
+        lse = np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)) + s.max(1)
+        p = np.exp(s - lse[:, None])
+        ds = c2 * (D + 2) * U * np.outer(np.linalg.norm(qi, axis=1), kn)
+        dlse = ds.max(1) + (N / 64 + 64) * U / math.log(2.0) + 4 * U
+        t = np.abs(s / math.log(2.0)) + np.abs(lse / math.log(2.0))[:, None]
+        rel = math.log(2.0) * (ds + dlse[:, None] + 2 * U * t) + 4 * U
+        A[a] = p.sum(0)
+        worst = max(worst, float(((p * rel).sum(0) / A[a]).max()) + 128 * U)
+    return A, worst
+
+
+@pytest.mark.parametrize("F,Hs,Ws,text,D", [(3, 6, 20, 10, 64), (2, 4, 100, 0, 128), (4, 16, 16, 0, 64)])
+def test_row_similarity_matches_oracle(F, Hs, Ws, text, D):
+    banner(f"row similarity F={F} Hs={Hs} Ws={Ws} D={D}")
+    N = F * Hs * Ws + text
+    q, k = _qk(1, 2, N, D, seed=F * 100 + Hs + Ws, spread=1.2)
+    s = svg.Shape(1, 2, N, D, F, Hs, Ws, 64)
+    scale = 1.0 / math.sqrt(D)
+    ws = torch.zeros(svg.svg_row_similarity_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    score = svg.svg_row_similarity(q.to(DEV), k.to(DEV), s, scale, workspace=ws).cpu().numpy()
+    torch.cuda.synchronize()
+    pats = ws[: 2 * F * Hs * N * 4].view(torch.float32).view(2, F * Hs, N).cpu().numpy()
+    for h in range(2):
+        qh, kh = q[0, h].float().numpy(), k[0, h].float().numpy()
+        ref, eps = _pattern_bound(qh, kh, scale, Ws, range(F * Hs))
+        assert (np.abs(pats[h] - ref) <= eps * ref + 1e-30).all(), f"head {h} patterns"
+        want = O.row_similarity(qh, kh, scale, F, Hs, Ws)
+        assert abs(score[h] - want) <= 4.1 * eps + 1e-9, (h, score[h], want, eps)
+
+
+def test_row_similarity_closed_forms():
+    banner("row similarity closed forms")
+    F, Hs, Ws, D = 2, 4, 8, 64
+    N = F * Hs * Ws
+    rng = np.random.default_rng(41)
+    # uniform attention: every row has the same pattern
+    k = torch.from_numpy(rng.standard_normal((1, 2, N, D))).to(torch.bfloat16)
+    q = torch.zeros_like(k)
+    # rows attending to their own orthonormal key direction: disjoint patterns
+    U_ = np.linalg.qr(rng.standard_normal((D, D)))[0][:, :F * Hs].T
+    rows = np.repeat(np.arange(F * Hs), Ws)
+    q[0, 1] = torch.from_numpy(U_[rows] * 60.0).to(torch.bfloat16)
+    k[0, 1] = torch.from_numpy(U_[rows]).to(torch.bfloat16)
+    s = svg.Shape(1, 2, N, D, F, Hs, Ws, 64)
+    score = svg.svg_row_similarity(q.to(DEV), k.to(DEV), s, 1.0).cpu().numpy()
+    torch.cuda.synchronize()
+    assert abs(score[0] - 1.0) < 1e-6 and abs(score[1]) < 1e-6, score
+
+
+def test_row_similarity_is_deterministic():
+    q, k = _qk(1, 2, 700, 128, seed=43)
+    s = svg.Shape(1, 2, 700, 128, 3, 5, 40, 128)
+    a = svg.svg_row_similarity(q.to(DEV), k.to(DEV), s, 0.09)
+    b = svg.svg_row_similarity(q.to(DEV), k.to(DEV), s, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_row_similarity_full_wan_shape_sampled(workload_inputs):
+    # two heads of the Wan 720p layer: each row pattern sums to Ws (its queries'
+    # weights sum to 1 each), sampled rows match the oracle, scores lie in [0, 1]
+    banner("row similarity wan720p sampled")
+    w, q, k, v, cls = workload_inputs("wan720p")
+    heads = [int(np.nonzero(cls == 0)[0][0]), int(np.nonzero(cls == 1)[0][0])]
+    qs = q[:, heads].contiguous()
+    ks = k[:, heads].contiguous()
+    s = svg.Shape(1, 2, w.N, w.D, w.F, w.Hs, w.Ws, w.block)
+    ws = torch.empty(svg.svg_row_similarity_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    score = svg.svg_row_similarity(qs.to(DEV), ks.to(DEV), s, w.scale, workspace=ws).cpu().numpy()
+    rows_n = w.F * w.Hs
+    pats = ws[: 2 * rows_n * w.N * 4].view(torch.float32).view(2, rows_n, w.N)
+    sums = pats.double().sum(2).cpu().numpy()
+    torch.cuda.synchronize()
+    assert ((score >= 0) & (score <= 1 + 1e-9)).all(), score
+    sample = [0, w.Hs - 1, rows_n // 2, rows_n - 1]
+    for a in range(2):
+        ref, eps = _pattern_bound(qs[0, a].float().numpy(), ks[0, a].float().numpy(), w.scale, w.Ws, sample)
+        got = pats[a, sample].cpu().numpy()
+        assert (np.abs(got - ref) <= eps * ref + 1e-30).all(), f"head {heads[a]}"
+        np.testing.assert_allclose(sums[a], w.Ws, rtol=eps)
