@@ -152,15 +152,11 @@ def main():
             ev[1].record(stream)
             layer.profile(q, k, v, idx[t % len(idx)])
             ev[2].record(stream)
-            for x, y in ((q, layer.qp), (k, layer.kp), (v, layer.vp)):
-                svg.svg_permute(x, s, layer.choice, inverse=False, out=y)
+            layer.permute_inputs(q, k, v)
             ev[3].record(stream)
-            svg.svg_block_sparse_attn(q, k, v, s, scale, layer.cand, head_mask=layer.choice,
-                                      head_layout=layer.choice, qp=layer.qp, kp=layer.kp,
-                                      vp=layer.vp, out=o, op=layer.op,
-                                      workspace=layer.attn_workspace)
+            layer.attend(q, k, v, out=o)
             ev[4].record(stream)
-            svg.svg_permute(layer.op, s, layer.choice, inverse=True, out=o)
+            layer.restore_output(o)
             ev[5].record(stream)
         else:
             ev[0].record(stream)
@@ -239,7 +235,8 @@ def main():
     }
     if w.mode == "online":
         tensor_bytes = w.N * w.D * 2
-        moved = 2 * 3 * n_temporal * tensor_bytes            # read + write of q, k, v
+        n_moved = 1 if layer.fused_layout else 3             # k only when Q, V, O go through the permutation in the attention
+        moved = 2 * n_moved * n_temporal * tensor_bytes      # read + write
         out["permute_gbs"] = round(moved / (per["permute"] * 1e-3) / 1e9, 1)
         out["permute_hbm_frac"] = round(out["permute_gbs"] / PEAK_HBM_GBS, 4)
         kv_bytes = 2 * w.B * w.H * tensor_bytes

@@ -202,8 +202,10 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
   if (svg_status st = check_shape(s, fn)) return st;
   if (svg_status st = check_head_dim(s, fn)) return st;
   if (!q || !k || !v || !o) return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / v / o", fn);
-  if (head_layout && (!qp || !kp || !vp || !op))
-    return fail(SVG_ERR_INVALID_ARG, "%s: head_layout given but a token-major twin is NULL", fn);
+  if (head_layout && !kp)
+    return fail(SVG_ERR_INVALID_ARG, "%s: head_layout given but kp is NULL", fn);
+  if (head_layout && s.block != 128 && (!qp || !vp || !op))
+    return fail(SVG_ERR_INVALID_ARG, "%s: 64-token blocks need all token-major twins with head_layout", fn);
   if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
   if (svg_status st = check_mask(masks, s, fn, 0)) return st;
   size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
@@ -234,6 +236,10 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
   a.vt = workspace;
   a.plan = nullptr;
   a.bitmap = masks->bitmap;
+  a.F = s.F;
+  a.S = s.Hs * s.Ws;
+  a.Nv = s.F * s.Hs * s.Ws;
+  a.divF = FastDiv(uint32_t(s.F > 0 ? s.F : 1));
   if (need > 0)
     a.plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                         (need - attn_plan_bytes(a.BH, (a.n_qb + 1) / 2)));

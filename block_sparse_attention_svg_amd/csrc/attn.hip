@@ -553,17 +553,23 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   const bool has_b = qb0 + 1 < a.n_qb;
 
   const int64_t head_off = int64_t(bh) * N * D;
-  const __bf16* Q = static_cast<const __bf16*>(tm ? a.qp : a.q) + head_off;
+  // a layout-1 head reads its Q rows from q and writes its O rows to o through
+  // the permutation when the token-major twin is not given
+  const bool gq = tm && a.qp == nullptr, so = tm && a.op == nullptr;
+  const __bf16* Q = static_cast<const __bf16*>(tm && !gq ? a.qp : a.q) + head_off;
   const char* Kh = reinterpret_cast<const char*>(static_cast<const __bf16*>(tm ? a.kp : a.k) + head_off);
-  __bf16* O = static_cast<__bf16*>(tm ? a.op : a.o) + head_off;
+  __bf16* O = static_cast<__bf16*>(tm && !so ? a.op : a.o) + head_off;
 
   const int q_row = (qb0 + grp) * C::BLK + w4 * 32 + n;
   bf16x8 qreg[C::DK];
+  {
+    const int q_src = gq && q_row < N ? frame_major_of(q_row, a) : q_row;
 #pragma unroll
-  for (int kk = 0; kk < C::DK; ++kk) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (q_row < N) u = *reinterpret_cast<const uint4*>(Q + int64_t(q_row) * D + 16 * kk + 8 * h);
-    qreg[kk] = as_bf16x8(u);
+    for (int kk = 0; kk < C::DK; ++kk) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (q_row < N) u = *reinterpret_cast<const uint4*>(Q + int64_t(q_src) * D + 16 * kk + 8 * h);
+      qreg[kk] = as_bf16x8(u);
+    }
   }
 
   // Copies of a group: wave w4 takes the tile's segments w4*PW .. w4*PW+PW-1.
@@ -733,7 +739,10 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = i * RPI + lane / LPR, c = lane % LPR;
       const uint4 x = *reinterpret_cast<const uint4*>(stage + r * RS + c * 16);
-      if (qrow0 + r < N) *reinterpret_cast<uint4*>(O + int64_t(qrow0 + r) * D + c * 8) = x;
+      if (qrow0 + r < N) {
+        const int dst = so ? frame_major_of(qrow0 + r, a) : qrow0 + r;
+        *reinterpret_cast<uint4*>(O + int64_t(dst) * D + c * 8) = x;
+      }
     }
   }
   if (q_row < N) {
@@ -951,19 +960,22 @@ template <int D>
 __global__ __launch_bounds__(256) void vt_prep_kernel(const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ vp,
                                                       const int32_t* __restrict__ head_layout,
-                                                      __bf16* __restrict__ vt, int N, int nKB) {
+                                                      __bf16* __restrict__ vt, int N, int nKB,
+                                                      AttnArgs a) {
   constexpr int BLK = 128, CPR = D / 8, TASKS = (BLK / 8) * CPR;
   const int kb = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
   if (t >= TASKS) return;
   const bool tm = head_layout && head_layout[bh] != 0;
-  const uint4* src = reinterpret_cast<const uint4*>((tm ? vp : v) + int64_t(bh) * N * D);
+  const bool gather = tm && vp == nullptr;   // token-major keys read from v through the permutation
+  const uint4* src = reinterpret_cast<const uint4*>((tm && !gather ? vp : v) + int64_t(bh) * N * D);
   const int dc = t % CPR, kg = t / CPR;
   uint4 rows[8], cols[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int key = kb * BLK + 8 * kg + i;
-    rows[i] = key < N ? src[int64_t(key) * CPR + dc] : make_uint4(0, 0, 0, 0);
+    const int row = gather && key < N ? frame_major_of(key, a) : key;
+    rows[i] = key < N ? src[int64_t(row) * CPR + dc] : make_uint4(0, 0, 0, 0);
   }
   transpose8x8(rows, cols);
   uint4* dst = reinterpret_cast<uint4*>(vt + (int64_t(bh) * nKB + kb) * BLK * D);
@@ -993,7 +1005,7 @@ template <int D>
 void launch_b128(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((vt_prep_kernel<D>), dim3(a.n_kb, a.BH), dim3(256), 0, st,
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.vp),
-                     a.head_layout, static_cast<__bf16*>(a.vt), a.N, a.n_kb);
+                     a.head_layout, static_cast<__bf16*>(a.vt), a.N, a.n_kb, a);
   const int pairs = (a.n_qb + 1) / 2;
   const int per_xcd = plan_range_cap(pairs);
   const int W = (a.n_kb + 31) / 32;

@@ -70,7 +70,17 @@ struct AttnArgs {
   void* vt;          // workspace: V of every head, block-transposed (128-key blocks)
   int32_t* plan;     // workspace: per head, 9 pair indices splitting its pairs over the XCDs
   const uint32_t* bitmap;  // [n_masks][n_qb][ceil(n_kb/32)]
+  // token-major index t < Nv is frame-major (t % F) * S + t / F (text tokens
+  // keep their index): used for layout-1 heads whose twin qp / vp / op is NULL
+  int F, S, Nv;
+  FastDiv divF;
 };
+// frame-major index of token-major index t
+__device__ __forceinline__ int frame_major_of(int t, const AttnArgs& a) {
+  if (t >= a.Nv) return t;
+  const int s = int(a.divF.div(uint32_t(t)));
+  return (t - s * a.F) * a.S + s;
+}
 size_t attn_workspace_bytes(int BH, int N, int D, int block);
 // Longest range of query-block pairs one XCD may take of a head: 1.5x the
 // even split (edge rows of banded masks carry less work), at least the even

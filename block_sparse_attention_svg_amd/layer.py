@@ -22,8 +22,12 @@ from .ops import (Shape, EncodedMasks, svg_build_masks, svg_encode_mask, svg_per
 
 
 class OnlineSparseAttention:
+    """fused_layout (128-token blocks): only K is moved to token-major order
+    by svg_permute; the attention reads the temporal heads' Q and V rows and
+    writes their O rows through the permutation, so no inverse move follows."""
+
     def __init__(self, s: Shape, band_w: int, scale: float = None, n_samples: int = 64,
-                 device="cuda"):
+                 device="cuda", fused_layout: bool = None):
         self.s = s
         self.scale = scale if scale is not None else 1.0 / math.sqrt(s.D)
         self.n_samples = n_samples
@@ -33,9 +37,11 @@ class OnlineSparseAttention:
                                      device=device)
         self.choice = torch.zeros(s.B * s.H, dtype=torch.int32, device=device)
         self.err = torch.zeros((s.B * s.H, 2), dtype=torch.float32, device=device)
+        self.fused_layout = (s.block == 128) if fused_layout is None else fused_layout
         shape = (s.B, s.H, s.N, s.D)
-        self.qp, self.kp, self.vp, self.op = (torch.empty(shape, dtype=torch.bfloat16, device=device)
-                                              for _ in range(4))
+        self.kp = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        self.qp, self.vp, self.op = (None, None, None) if self.fused_layout else (
+            torch.empty(shape, dtype=torch.bfloat16, device=device) for _ in range(3))
         self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s), 1), dtype=torch.uint8,
                                           device=device)
 
@@ -43,16 +49,28 @@ class OnlineSparseAttention:
         return svg_profile_heads(q, k, v, self.s, self.scale, idx, self.cand, self.workspace,
                                  self.choice, self.err)
 
-    def __call__(self, q, k, v, idx, out=None, lse=False):
-        s = self.s
-        self.profile(q, k, v, idx)
+    def permute_inputs(self, q, k, v):
+        """Token-major twins of the temporal heads (K only when fused)."""
         for x, y in ((q, self.qp), (k, self.kp), (v, self.vp)):
-            svg_permute(x, s, self.choice, inverse=False, out=y)
-        out, _, lse_t = svg_block_sparse_attn(q, k, v, s, self.scale, self.cand,
-                                              head_mask=self.choice, head_layout=self.choice,
-                                              qp=self.qp, kp=self.kp, vp=self.vp, out=out,
-                                              op=self.op, lse=lse, workspace=self.attn_workspace)
-        svg_permute(self.op, s, self.choice, inverse=True, out=out)
+            if y is not None:
+                svg_permute(x, self.s, self.choice, inverse=False, out=y)
+
+    def attend(self, q, k, v, out=None, lse=False):
+        return svg_block_sparse_attn(q, k, v, self.s, self.scale, self.cand,
+                                     head_mask=self.choice, head_layout=self.choice,
+                                     qp=self.qp, kp=self.kp, vp=self.vp, out=out,
+                                     op=self.op, lse=lse, workspace=self.attn_workspace)
+
+    def restore_output(self, out):
+        """Frame-major output of the temporal heads (nothing to do when fused)."""
+        if self.op is not None:
+            svg_permute(self.op, self.s, self.choice, inverse=True, out=out)
+
+    def __call__(self, q, k, v, idx, out=None, lse=False):
+        self.profile(q, k, v, idx)
+        self.permute_inputs(q, k, v)
+        out, _, lse_t = self.attend(q, k, v, out=out, lse=lse)
+        self.restore_output(out)
         return out, lse_t
 
 

@@ -161,7 +161,11 @@ def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
                           head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
                           qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False,
                           workspace: torch.Tensor = None):
-    """Block-sparse attention; returns (o, op, lse or None)."""
+    """Block-sparse attention; returns (o, op, lse or None).
+
+    With head_layout, kp is required; qp, vp and op may be None (128-token
+    blocks): layout-1 heads then read Q / V from q / v and write O to `out`
+    through the permutation, and the returned op is None."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need_act(t, n, s)
     if out is None:
@@ -169,11 +173,10 @@ def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
     _need_act(out, "out", s)
     if head_layout is not None:
         _need(head_layout, "head_layout", torch.int32)
-        for t, n in ((qp, "qp"), (kp, "kp"), (vp, "vp")):
-            _need_act(t, n, s)
-        if op is None:
-            op = torch.empty_like(q)
-        _need_act(op, "op", s)
+        _need_act(kp, "kp", s)
+        for t, n in ((qp, "qp"), (vp, "vp"), (op, "op")):
+            if t is not None:
+                _need_act(t, n, s)
     if head_mask is not None:
         _need(head_mask, "head_mask", torch.int32)
     lse_t = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=q.device) if lse else None

@@ -142,7 +142,13 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  * key blocks are read.  Not causal.
  *   q, k, v, o     : bf16 [B,H,N,D] frame-major.
  *   qp, kp, vp, op : bf16 [B,H,N,D] token-major twins; may be NULL when no
- *                    head uses layout 1.
+ *                    head uses layout 1.  With 128-token blocks only kp is
+ *                    required: a layout-1 head whose qp / vp / op is NULL
+ *                    reads its Q / V rows from q / v and writes its O rows
+ *                    to o through the permutation (token-major row t is
+ *                    frame-major row (t % F)*Hs*Ws + t / F, text rows in
+ *                    place), so those tensors need no separate svg_permute
+ *                    and o holds every head frame-major.
  *   masks          : host struct; n_qb == n_kb == ceil(N/block); with
  *                    128-token blocks at most 131070 blocks and 32768 masks
  *                    (SVG_ERR_UNSUPPORTED beyond).

@@ -32,7 +32,8 @@ def _run_heads(w, q, k, v, masks_np, layout, block=None, lse=False):
     hm = torch.arange(len(layout), dtype=torch.int32, device=DEV)
     qp, kp, vp = (svg.svg_permute(t, s, lay) for t in (qd, kd, vd))
     o, op, lse_t = svg.svg_block_sparse_attn(qd, kd, vd, s, 1.0 / np.sqrt(w.D), enc, head_mask=hm,
-                                             head_layout=lay, qp=qp, kp=kp, vp=vp, lse=lse)
+                                             head_layout=lay, qp=qp, kp=kp, vp=vp,
+                                             op=torch.empty_like(qd), lse=lse)
     torch.cuda.synchronize()
     return o, op, lse_t
 
@@ -257,3 +258,32 @@ def test_softmax_reference_moves(order):
     assert np.all(np.isfinite(to_np(o[0, 0])))
     assert_attn_close(to_np(o[0, 0]), ref, f"reference {order}")
     assert np.max(np.abs(lse[0, 0].cpu().numpy() - ref_lse)) < LSE_ABS * max(1.0, float(np.max(np.abs(ref_lse))) / 64)
+
+
+def test_fused_layout_equals_permuted_twins():
+    """Layout-1 heads reading Q / V and writing O through the permutation give
+    the same bits as the separate svg_permute moves (same arithmetic, only the
+    addressing differs); a text tail keeps its rows; LSE stays token-major."""
+    banner("attn fused layout")
+    F, Hs, Ws, text, D, H = 3, 5, 40, 70, 128, 4
+    N = F * Hs * Ws + text
+    g = torch.Generator().manual_seed(77)
+    q, k, v = (torch.randn(1, H, N, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    s = svg.Shape(1, H, N, D, F, Hs, Ws, 128)
+    nB = s.n_blocks
+    rng = np.random.default_rng(78)
+    M = (rng.random((H, nB, nB)) < 0.5).astype(np.uint8)
+    M[np.arange(H), :, nB - 1] = 1
+    enc = svg.svg_encode_mask(torch.from_numpy(M).to(DEV))
+    lay = torch.tensor([0, 1, 1, 0], dtype=torch.int32, device=DEV)
+    hm = torch.arange(H, dtype=torch.int32, device=DEV)
+    qp, kp, vp = (svg.svg_permute(t, s, lay) for t in (q, k, v))
+    o_t, op, lse_t = svg.svg_block_sparse_attn(q, k, v, s, 0.09, enc, head_mask=hm, head_layout=lay,
+                                               qp=qp, kp=kp, vp=vp, op=torch.empty_like(q), lse=True)
+    svg.svg_permute(op, s, lay, inverse=True, out=o_t)
+    o_f, op_f, lse_f = svg.svg_block_sparse_attn(q, k, v, s, 0.09, enc, head_mask=hm, head_layout=lay,
+                                                 kp=kp, lse=True)
+    torch.cuda.synchronize()
+    assert op_f is None
+    assert torch.equal(o_t, o_f)
+    assert torch.equal(lse_t, lse_f)
