@@ -226,7 +226,10 @@ def main():
         "data": "synthetic (seeded generator; no model weights)",
         "config": {"workload": describe(w), "heads_temporal": n_temporal,
                    "heads_spatial": w.H - n_temporal, "profiler_samples": w.n_samples,
-                   "attention_gflop": round(flop / 1e9, 2)},
+                   "attention_gflop": round(flop / 1e9, 2),
+                   "layout": (("K moved by svg_permute; Q, V, O of temporal heads through the permutation "
+                               "inside the attention call") if w.mode == "online" and layer.fused_layout
+                              else "svg_permute of q, k, v and of op" if w.mode == "online" else "frame-major")},
         "ms_per_call": {n: round(v, 4) for n, v in per.items()},
         "attention_tflops": round(achieved, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
