@@ -386,15 +386,26 @@ __device__ __forceinline__ void barrier_lds_only() {
 
 // Builds window w from the bitmap rows bm0 (row 0) and bm0 + W (row 1, read
 // only when `two`); every thread of the workgroup calls it (it synchronizes).
-__device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict__ bm0, bool two,
-                                          int W, int w) {
+// The two rows' bitmap words of window w for thread tid < 64 (its word of
+// the window), requested before the caller's other loads so that they return
+// first.
+__device__ __forceinline__ uint2 seq_words(const uint32_t* __restrict__ bm0, bool two, int W, int w) {
+  const int tid = threadIdx.x;
+  uint2 r = make_uint2(0u, 0u);
+  if (tid < 64) {
+    const int word = kSeqWords * w + tid;
+    r.x = word < W ? bm0[word] : 0u;
+    r.y = two && word < W ? bm0[W + word] : 0u;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void seq_scan(SeqLds& L, uint2 words, int W, int w) {
   const int tid = threadIdx.x;
   const int kb0 = 32 * kSeqWords * w;
   barrier_lds_only();   // the previous window is no longer read
   if (tid < 64) {
-    const int word = kSeqWords * w + tid;
-    const uint32_t a = word < W ? bm0[word] : 0u;
-    const uint32_t b = two && word < W ? bm0[W + word] : 0u;
+    const uint32_t a = words.x, b = words.y;
     const uint32_t u = a | b;
     const int c = __builtin_popcount(u);
     int incl = c;   // inclusive prefix sum over the wave
@@ -412,6 +423,11 @@ __device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict_
     if (tid == 0) L.seq[total] = (w + 1) * kSeqWords < W ? kSeqRefill : kSeqEnd;
   }
   barrier_lds_only();
+}
+
+__device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict__ bm0, bool two,
+                                          int W, int w) {
+  seq_scan(L, seq_words(bm0, two, W, w), W, w);
 }
 
 // S^T (128 keys x 32 queries) = K Q^T.  The scheduling barriers keep the K
@@ -561,6 +577,11 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   __bf16* O = static_cast<__bf16*>(tm && !so ? a.op : a.o) + head_off;
 
   const int q_row = (qb0 + grp) * C::BLK + w4 * 32 + n;
+  // the item's block list needs its mask rows first: their words are
+  // requested ahead of the Q rows
+  const int W = (a.n_kb + 31) >> 5;
+  const uint32_t* bm0 = a.bitmap + (int64_t(mask_id) * a.n_qb + qb0) * W;
+  const uint2 words0 = seq_words(bm0, has_b, W, 0);
   bf16x8 qreg[C::DK];
   {
     const int q_src = gq && q_row < N ? frame_major_of(q_row, a) : q_row;
@@ -614,10 +635,8 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   bf16x8 pb[C::PS];
 
   __shared__ SeqLds sl;
-  const int W = (a.n_kb + 31) >> 5;
-  const uint32_t* bm0 = a.bitmap + (int64_t(mask_id) * a.n_qb + qb0) * W;
   int seq_w = 0, seq_j = 1;
-  seq_build(sl, bm0, has_b, W, 0);
+  seq_scan(sl, words0, W, 0);
   uint32_t seq_v = sl.seq[0];   // next entry, read one call ahead
   // Next block of the merged sequence; `mine` = my row keeps it.  All waves
   // call this at the same points, so a window refill may synchronize.
