@@ -3,8 +3,8 @@
 // skip list of kept intervals; [VDA] section 5.3: tiled attention with an
 // online softmax so the N x N score matrix never reaches memory).
 //
-// One workgroup per (batch*head, query block); BLK/32 wavefronts, each owning
-// 32 queries.  Per kept key block:
+// 64-token blocks: one workgroup per (batch*head, query block); BLK/32
+// wavefronts, each owning 32 queries.  Per kept key block:
 //   * the whole workgroup stages K (row-major) and V (transposed to V^T) in
 //     LDS; the next block's global loads are issued before the current block
 //     is computed, so they overlap with the MFMA work;
@@ -281,8 +281,13 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_fwd_kernel(AttnArgs a) {
 // copies for the LDS, and the waves running MFMAs never issue one.  V^T comes
 // from a per-block transposed workspace, so both operands are read with
 // plain 16-byte LDS fetches.  The merged key-block sequence of the two rows
-// is built in LDS once per 2048 key blocks, so choosing the next block is
-// one LDS read.
+// (their union, from the mask bitmap) is built in LDS once per 2048 key
+// blocks, so choosing the next block is one LDS read.
+//
+// Workgroups are persistent, one per CU, and take their pairs of query blocks
+// from per-XCD work queues (see attn_fwd_b128_kernel).  A layout-1 head whose
+// token-major Q / V / O twin is not given reads Q and V from the frame-major
+// tensors and writes O to them through the layout permutation.
 // ---------------------------------------------------------------------------
 #define LDS_AS __attribute__((address_space(3)))
 
