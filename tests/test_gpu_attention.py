@@ -287,3 +287,58 @@ def test_fused_layout_equals_permuted_twins():
     assert op_f is None
     assert torch.equal(o_t, o_f)
     assert torch.equal(lse_t, lse_f)
+
+
+def test_many_small_heads_through_the_work_queues():
+    """300 heads of 700 tokens (3 pairs of query blocks each, 900 work items
+    for 256 persistent workgroups): every XCD's queue drains and the
+    workgroups take items from the other queues; sampled heads against the
+    oracle, and a second call gives the same bits."""
+    banner("attn many small heads")
+    H, N, D = 300, 700, 64
+    g = torch.Generator().manual_seed(91)
+    q, k, v = (torch.randn(1, H, N, D, generator=g).to(torch.bfloat16) for _ in range(3))
+    s = svg.Shape(1, H, N, D, 1, 1, N, 128)
+    nB = s.n_blocks
+    rng = np.random.default_rng(92)
+    M = (rng.random((7, nB, nB)) < 0.6).astype(np.uint8)
+    M[:, :, 0] = 1
+    enc = svg.svg_encode_mask(torch.from_numpy(M).to(DEV))
+    hm = torch.from_numpy(rng.integers(0, 7, H).astype(np.int32)).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, _, lse1 = svg.svg_block_sparse_attn(qd, kd, vd, s, 0.125, enc, head_mask=hm, lse=True)
+    o2, _, lse2 = svg.svg_block_sparse_attn(qd, kd, vd, s, 0.125, enc, head_mask=hm, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    hmn = hm.cpu().numpy()
+    for h in [0, 1, 150, 257, 299]:
+        ref, ref_lse = O.block_masked_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
+                                                v[0, h].float().numpy(), M[hmn[h]], 128, 0.125)
+        assert_attn_close(to_np(o1[0, h]), ref, f"small head {h}")
+        assert np.max(np.abs(lse1[0, h].cpu().numpy() - ref_lse)) < LSE_ABS
+
+
+def test_fused_layout_batch2_mixed_layouts():
+    """B = 2 with a text tail and per-(batch, head) layouts: the fused layout
+    gives the bits of the separate permutation moves."""
+    banner("attn fused layout batch2")
+    B, H, F, Hs, Ws, text, D = 2, 3, 4, 6, 24, 33, 128
+    N = F * Hs * Ws + text
+    g = torch.Generator().manual_seed(93)
+    q, k, v = (torch.randn(B, H, N, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    s = svg.Shape(B, H, N, D, F, Hs, Ws, 128)
+    nB = s.n_blocks
+    rng = np.random.default_rng(94)
+    M = (rng.random((2, nB, nB)) < 0.5).astype(np.uint8)
+    M[:, :, nB - 1] = 1
+    enc = svg.svg_encode_mask(torch.from_numpy(M).to(DEV))
+    lay = torch.tensor([1, 0, 1, 1, 1, 0], dtype=torch.int32, device=DEV)
+    qp, kp, vp = (svg.svg_permute(t, s, lay) for t in (q, k, v))
+    o_t, op, lse_t = svg.svg_block_sparse_attn(q, k, v, s, 0.09, enc, head_mask=lay, head_layout=lay,
+                                               qp=qp, kp=kp, vp=vp, op=torch.empty_like(q), lse=True)
+    svg.svg_permute(op, s, lay, inverse=True, out=o_t)
+    o_f, _, lse_f = svg.svg_block_sparse_attn(q, k, v, s, 0.09, enc, head_mask=lay, head_layout=lay,
+                                              kp=kp, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_t, o_f)
+    assert torch.equal(lse_t, lse_f)
