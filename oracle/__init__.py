@@ -10,6 +10,9 @@ Sources cited in the modules:
   [CalibAtt] calibrated sparse attention article (lpnh.cn/news/568491)
   [VDA]      video-diffusion acceleration survey (wmrh.cn/news/48564)
   [SparsePR] SparsePR tutorial (lqnn.cn/news/72918)
+  RMSNorm: Zhang & Sennrich, "Root Mean Square Layer Normalization" (2019)
+  RoPE:    Su et al., "RoFormer: Enhanced Transformer with Rotary Position
+           Embedding" (2021)
 
 Every function here is pinned by a CPU test to facts other than itself; none is
 "parity unpinned".
@@ -25,6 +28,7 @@ from .profiler import profile_heads, profile_errors_decomposed
 from .calibrate import calibrate_row, calibrate_mask, block_energy, eps_schedule, aggregate_masks
 from .broadcast import row_broadcast, row_patterns, row_similarity, is_row_repetitive
 from .flops import kept_pairs, algorithmic_flops
+from .norm_rope import rms_norm, rope_angles, rope_rotate, qk_norm_rope
 
 __all__ = [
     "token_major_index", "to_token_major", "to_frame_major",
@@ -35,4 +39,5 @@ __all__ = [
     "profile_heads", "profile_errors_decomposed",
     "calibrate_row", "calibrate_mask", "block_energy", "eps_schedule", "aggregate_masks", "row_broadcast", "row_patterns", "row_similarity", "is_row_repetitive",
     "kept_pairs", "algorithmic_flops",
+    "rms_norm", "rope_angles", "rope_rotate", "qk_norm_rope",
 ]
