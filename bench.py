@@ -106,6 +106,78 @@ def cpu_baseline(w, q, k, v, classes, budget_s):
                        f"host has {os.cpu_count()} cores")}
 
 
+def norm_rope_leg(w, s, classes, dev, stream, reps=20):
+    """QK-Norm + 3D RoPE of one projection tensor (query or key rows) into the
+    attention input, each head in its layout, timed over `reps` calls after a
+    warm-up; beside it the same arithmetic as plain PyTorch eager ops (the
+    pages' comparison point), its cos / sin table built outside the timing."""
+    import torch
+    import synth
+    import block_sparse_attention_svg_amd as svg
+
+    x = synth.gen_projection_rows(w.B, w.N, w.H, w.D, seed=w.seed + 5, device=dev)
+    gamma = torch.from_numpy(synth.gen_norm_weight(w.H * w.D, w.seed + 6)).to(dev)
+    third = w.D // 6
+    rope = (w.D - 4 * third, 2 * third, 2 * third, 10000.0)
+    lay = torch.from_numpy(np.tile(classes.astype(np.int32), w.B)).to(dev)
+    y = svg.svg_qk_norm_rope(x, s, norm="row", gamma=gamma, rope=rope, head_layout=lay)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        svg.svg_qk_norm_rope(x, s, norm="row", gamma=gamma, rope=rope, head_layout=lay, out=y)
+    e0.record(stream)
+    for _ in range(reps):
+        svg.svg_qk_norm_rope(x, s, norm="row", gamma=gamma, rope=rope, head_layout=lay, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * x.numel() * x.element_size()              # read x once, write y once
+
+    # plain PyTorch: fp32 norm, rotation by a cached table, transpose, layout gather
+    S_ = w.Hs * w.Ws
+    n = torch.arange(w.N, device=dev)
+    f, sp = n // S_, n % S_
+    pos = [f, sp // w.Ws, sp % w.Ws]
+    ang = []
+    for p_, d in zip(pos, rope[:3]):
+        fr = rope[3] ** (-2.0 * torch.arange(d // 2, device=dev, dtype=torch.float64) / d)
+        ang.append(p_[:, None].double() * fr[None, :])
+    ang = torch.cat(ang, 1)
+    ang[n >= w.F * S_] = 0
+    cos, sin = ang.cos().float(), ang.sin().float()
+    tm = torch.arange(w.N, device=dev)
+    tm[: w.F * S_] = (sp * w.F + f)[: w.F * S_]
+    g2 = gamma.view(w.H, w.D)
+
+    def eager():
+        xf = x.float()
+        xn = xf * torch.rsqrt(xf.pow(2).mean(dim=(-2, -1), keepdim=True) + 1e-6) * g2
+        a_, b_ = xn[..., 0::2], xn[..., 1::2]
+        c_, s_ = cos[None, :, None, :], sin[None, :, None, :]
+        r = torch.stack((a_ * c_ - b_ * s_, a_ * s_ + b_ * c_), -1).flatten(-2)
+        r = r.to(torch.bfloat16).transpose(1, 2).contiguous()
+        out = torch.empty_like(r)
+        sel = lay.view(w.B, w.H).bool()
+        out[~sel] = r[~sel]
+        rs = r[sel]
+        out[sel] = torch.empty_like(rs).index_copy_(1, tm, rs)
+        return out
+
+    ref = eager()
+    e0.record(stream)
+    for _ in range(3):
+        eager()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_ms = e0.elapsed_time(e1) / 3
+    diff = (ref.float() - y.float()).abs().max().item()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes": nbytes, "torch_eager_ms": round(t_ms, 3), "speedup_vs_torch": round(t_ms / ms, 1),
+            "max_abs_diff_vs_torch": round(diff, 4),
+            "note": "one tensor (query or key rows) [B,N,H,D] -> [B,H,N,D]: RMS over the H*D row, "
+                    f"rope runs {rope[:3]}, theta 1e4, temporal heads token-major; not part of the layer step"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +317,7 @@ def main():
         kv_bytes = 2 * w.B * w.H * tensor_bytes
         out["profile_gbs"] = round(kv_bytes / (per["profile"] * 1e-3) / 1e9, 1)
         out["profile_share"] = round(per["profile"] / ms_step, 4)
+        out["qk_norm_rope"] = norm_rope_leg(w, s, classes, dev, stream)
     if w.mode == "static":
         # offline calibration's block-energy pass over every head, timed once
         # after a warm-up call (not part of the layer step)

@@ -1,7 +1,7 @@
 """Block-sparse 3D attention for video diffusion transformers on MI355X (gfx950).
 
 Spatial / temporal head masks, the frame-major <-> token-major layout
-permutation, sampled-query online head profiling and calibrated static masks
+permutation, the fused QK-Norm + 3D RoPE step before the attention, sampled-query online head profiling and calibrated static masks
 encoded as bitmap + skip list, all computed by the HIP kernels of libsvg.so
 behind the C ABI in include/svg.h.  This package is the thin Python binding.
 """
@@ -11,7 +11,7 @@ from .ops import (
     svg_profile_workspace_bytes, svg_profile_heads, svg_attn_workspace_bytes,
     svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows, svg_calibrate_masks, svg_version,
     svg_block_energy, svg_aggregate_masks, svg_eps_schedule, svg_row_similarity,
-    svg_row_similarity_workspace_bytes,
+    svg_row_similarity_workspace_bytes, svg_qk_norm_rope,
 )
 from .layer import OnlineSparseAttention, StaticSparseAttention, attention_flops, kept_pairs_per_mask
 from ._lib import SvgError, LIB_PATH
@@ -22,7 +22,7 @@ __all__ = [
     "svg_block_sparse_attn",
     "svg_row_broadcast", "svg_restrict_anchor_rows", "svg_calibrate_masks", "svg_version",
     "svg_block_energy", "svg_aggregate_masks", "svg_eps_schedule", "svg_row_similarity",
-    "svg_row_similarity_workspace_bytes",
+    "svg_row_similarity_workspace_bytes", "svg_qk_norm_rope",
     "OnlineSparseAttention", "StaticSparseAttention", "attention_flops", "kept_pairs_per_mask",
     "SvgError", "LIB_PATH",
 ]

@@ -26,6 +26,11 @@ class SvgMask(ctypes.Structure):
     ]
 
 
+class SvgRope(ctypes.Structure):
+    _fields_ = [("d_f", ctypes.c_int), ("d_y", ctypes.c_int), ("d_x", ctypes.c_int),
+                ("theta", ctypes.c_float)]
+
+
 class SvgError(RuntimeError):
     def __init__(self, fn, status, msg):
         super().__init__(f"{fn} failed with status {status}: {msg}")
@@ -39,6 +44,7 @@ _SIGS = {
     "svg_encode_iv_capacity": (ctypes.c_int64, [_I, _I, _I]),
     "svg_encode_mask": (_I, [_P, _I, _I, _I, _P, _P, _P, ctypes.c_int64, _P]),
     "svg_permute": (_I, [_P, _P, _I, SvgShape, _P, _I, _P]),
+    "svg_qk_norm_rope": (_I, [_P, _P, SvgShape, _I, _P, ctypes.c_float, ctypes.POINTER(SvgRope), _P, _P]),
     "svg_profile_workspace_bytes": (ctypes.c_size_t, [SvgShape, _I]),
     "svg_profile_heads": (_I, [_P, _P, _P, SvgShape, ctypes.c_float, _P, _I,
                                ctypes.POINTER(SvgMask), _P, _P, _P, ctypes.c_size_t, _P]),

@@ -148,6 +148,40 @@ svg_status svg_permute(const void* x, void* y, svg_dtype dt, svg_shape s, const 
   return check_launch(fn);
 }
 
+svg_status svg_qk_norm_rope(const void* x, void* y, svg_shape s, int norm_span, const float* gamma,
+                            float eps, const svg_rope* rope, const int32_t* head_layout,
+                            void* stream) {
+  const char* fn = "svg_qk_norm_rope";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (!x || !y) return fail(SVG_ERR_INVALID_ARG, "%s: x or y is NULL", fn);
+  if (s.H * s.D > 8192)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: H*D = %d exceeds 8192", fn, s.H * s.D);
+  size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
+  if (overlaps(x, y, bytes)) return fail(SVG_ERR_INVALID_ARG, "%s: x and y overlap", fn);
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: x and y must be 16-byte aligned", fn);
+  if (norm_span < 0 || norm_span > 2)
+    return fail(SVG_ERR_INVALID_ARG, "%s: norm_span must be 0, 1 or 2 (got %d)", fn, norm_span);
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(SVG_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (gamma && (reinterpret_cast<uintptr_t>(gamma) & 15))
+    return fail(SVG_ERR_INVALID_ARG, "%s: gamma must be 16-byte aligned", fn);
+  if (rope) {
+    const int d[3] = {rope->d_f, rope->d_y, rope->d_x};
+    for (int i = 0; i < 3; ++i)
+      if (d[i] < 0 || (d[i] & 1))
+        return fail(SVG_ERR_INVALID_ARG, "%s: rope runs must be even and >= 0", fn);
+    if (d[0] + d[1] + d[2] != s.D)
+      return fail(SVG_ERR_INVALID_ARG, "%s: rope runs sum to %d, not D = %d", fn, d[0] + d[1] + d[2],
+                  s.D);
+    if (!(rope->theta > 0.f) || !std::isfinite(rope->theta))
+      return fail(SVG_ERR_INVALID_ARG, "%s: rope theta must be finite and > 0", fn);
+  }
+  launch_norm_rope(x, y, s, norm_span, gamma, eps, rope, head_layout, as_stream(stream));
+  return check_launch(fn);
+}
+
 size_t svg_profile_workspace_bytes(svg_shape s, int n_samples) {
   if (check_shape(s, "svg_profile_workspace_bytes") != SVG_OK) return 0;
   return profile_workspace_bytes(s.B * s.H, s.N, s.D, s.block, n_samples, nullptr, nullptr);

@@ -51,6 +51,8 @@ void launch_encode(const uint8_t* dense, int n_masks, int n_qb, int n_kb, uint32
                    int32_t* row_ptr, int32_t* iv, hipStream_t st);
 void launch_permute(const void* x, void* y, int elem_bytes, const svg_shape& s,
                     const int32_t* head_sel, int inverse, hipStream_t st);
+void launch_norm_rope(const void* x, void* y, const svg_shape& s, int norm_span, const float* gamma,
+                      float eps, const svg_rope* rope, const int32_t* head_layout, hipStream_t st);
 void launch_row_broadcast(void* o, const svg_shape& s, const int32_t* head_sel, int k,
                           hipStream_t st);
 

@@ -126,6 +126,43 @@ def svg_permute(x: torch.Tensor, s: Shape, head_sel: torch.Tensor = None, invers
     return out
 
 
+_NORM_SPAN = {None: 0, "head": 1, "row": 2}
+
+
+def svg_qk_norm_rope(x: torch.Tensor, s: Shape, norm: str = "head", gamma: torch.Tensor = None,
+                     eps: float = 1e-6, rope=None, head_layout: torch.Tensor = None,
+                     out: torch.Tensor = None) -> torch.Tensor:
+    """Projection rows x [B, N, H, D] -> attention input [B, H, N, D], RMS
+    normalised over each head (norm="head") or the whole row (norm="row") or
+    not at all (None), turned by the 3D rotary embedding rope = (d_f, d_y, d_x,
+    theta) or not (None), each head written in its layout (head_layout [B*H],
+    1 = token-major; None = all frame-major)."""
+    if norm not in _NORM_SPAN:
+        raise ValueError(f"norm must be None, 'head' or 'row' (got {norm!r})")
+    if tuple(x.shape) != (s.B, s.N, s.H, s.D) or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError(f"x must be contiguous bfloat16 [{s.B}, {s.N}, {s.H}, {s.D}]")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if out is None:
+        out = torch.empty((s.B, s.H, s.N, s.D), dtype=torch.bfloat16, device=x.device)
+    _need_act(out, "out", s)
+    if gamma is not None:
+        _need(gamma, "gamma", torch.float32)
+        want = s.D if norm == "head" else s.H * s.D
+        if gamma.numel() != want:
+            raise ValueError(f"gamma must hold {want} values for norm={norm!r}")
+    if head_layout is not None:
+        _need(head_layout, "head_layout", torch.int32)
+    r = None
+    if rope is not None:
+        d_f, d_y, d_x, theta = rope
+        r = ctypes.byref(L.SvgRope(int(d_f), int(d_y), int(d_x), float(theta)))
+    L.check("svg_qk_norm_rope", L.lib().svg_qk_norm_rope(
+        _ptr(x), _ptr(out), s.c(), _NORM_SPAN[norm], _ptr(gamma), float(eps), r, _ptr(head_layout),
+        _stream()))
+    return out
+
+
 def svg_profile_workspace_bytes(s: Shape, n_samples: int) -> int:
     return int(L.lib().svg_profile_workspace_bytes(s.c(), n_samples))
 

@@ -110,6 +110,40 @@ svg_status svg_encode_mask(const uint8_t* dense, int n_masks, int n_qb, int n_kb
 svg_status svg_permute(const void* x, void* y, svg_dtype dt, svg_shape s,
                        const int32_t* head_sel, int inverse, void* stream);
 
+/* ---- step before the attention: QK-Norm + 3D RoPE ------------------------ */
+/* Rotary embedding split over the video grid: channel pairs [0, d_f/2) turn
+ * with the frame index, the next d_y/2 with the row, the last d_x/2 with the
+ * column; pair i of a run of d channels turns by pos * theta^(-2i/d) rad
+ * (RoFormer, Su et al. 2021).  d_f, d_y, d_x even and >= 0, summing to D. */
+typedef struct {
+  int d_f, d_y, d_x;
+  float theta;      /* frequency base, > 0 (10000 in most video DiTs) */
+} svg_rope;
+
+/* QK-Norm and RoPE of query or key rows, written straight into the attention
+ * input in each head's layout ([SVG], "Layout Transformation + Kernel": the
+ * custom QK-Norm and RoPE kernels that precede the sparse attention).
+ *   x          : bf16 [B,N,H,D], the projection output, frame-major tokens.
+ *   y          : bf16 [B,H,N,D] out; must not overlap x.
+ *   norm_span  : 0 no normalisation, 1 RMS over each head's D channels, 2 RMS
+ *                over the whole H*D row (Zhang & Sennrich 2019, no centring):
+ *                x / sqrt(mean(x^2) + eps) * gamma.
+ *   gamma      : device float [D] (norm_span 1) or [H*D] (norm_span 2),
+ *                16-byte aligned, or NULL for all ones.  eps >= 0.
+ *   rope       : host struct, or NULL for no rotation.  Video token
+ *                n = f*Hs*Ws + yy*Ws + xx sits at (f, yy, xx); text tokens
+ *                (n >= F*Hs*Ws) are not rotated.
+ *   head_layout: device int32 [B*H], or NULL for all 0: heads with 1 are
+ *                written token-major (video token f*S + s at row s*F + f,
+ *                S = Hs*Ws), the rest frame-major.
+ * fp32 arithmetic from the exact inputs, one rounding to bf16 (nearest even).
+ * With norm_span 0 and rope NULL the call is an exact transpose / layout move
+ * (V of a layer).  s.block is not read but must be valid.  x, y 16-byte
+ * aligned; D in {64, 128}; H*D <= 8192 (SVG_ERR_UNSUPPORTED otherwise). */
+svg_status svg_qk_norm_rope(const void* x, void* y, svg_shape s, int norm_span, const float* gamma,
+                            float eps, const svg_rope* rope, const int32_t* head_layout,
+                            void* stream);
+
 /* ---- a3: online head profiling ------------------------------------------ */
 /* Workspace size in bytes for svg_profile_heads (host function). */
 size_t svg_profile_workspace_bytes(svg_shape s, int n_samples);

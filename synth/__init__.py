@@ -14,9 +14,12 @@ from .generate import (
     energy_matrix,
     repetitive_heads,
     to_bf16,
+    gen_projection_rows,
+    gen_norm_weight,
 )
 
 __all__ = [
     "CONFIGS", "Workload", "get_workload", "head_classes", "gen_head_qkv",
     "gen_qkv", "sample_query_idx", "energy_matrix", "repetitive_heads", "to_bf16",
+    "gen_projection_rows", "gen_norm_weight",
 ]

@@ -135,3 +135,20 @@ def repetitive_heads(w: Workload) -> np.ndarray:
         return np.zeros(0, dtype=np.int32)
     rng = np.random.default_rng(w.seed * 7 + 3)
     return np.sort(rng.choice(w.H, size=w.n_repetitive, replace=False)).astype(np.int32)
+
+
+def gen_projection_rows(B: int, N: int, H: int, D: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Seeded bf16 [B, N, H, D] query / key projection rows (frame-major tokens):
+    standard normal entries times a per-head scale drawn log-uniformly from
+    [1/4, 4] and a per-token scale from [1/2, 2], so that RMS normalisation has
+    rows of different size to equalise."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn((B, N, H, D), generator=g, device=device, dtype=torch.float32)
+    hs = torch.exp(torch.rand(H, generator=g, device=device) * (2 * math.log(4.0)) - math.log(4.0))
+    ts = torch.exp(torch.rand((B, N), generator=g, device=device) * (2 * math.log(2.0)) - math.log(2.0))
+    return (x * ts[:, :, None, None] * hs[None, None, :, None]).to(torch.bfloat16)
+
+
+def gen_norm_weight(n: int, seed: int = 0) -> np.ndarray:
+    """Seeded float32 norm weights, uniform in [0.5, 1.5]."""
+    return np.random.default_rng(seed).uniform(0.5, 1.5, n).astype(np.float32)

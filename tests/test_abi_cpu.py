@@ -195,3 +195,26 @@ def test_calibration_validation():
     assert lib.svg_row_similarity(FAKE, FAKE, _shape(Ws=256, N=4 * 16 * 256), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
     assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=1, Ws=256, N=1024), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
     assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=65, Ws=4, N=1040), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
+
+
+def test_qk_norm_rope_validation():
+    lib = L.lib()
+    s = _shape()
+    y = ctypes.c_void_p(1 << 40)
+    ok_rope = L.SvgRope(s.D - 64, 32, 32, 10000.0)
+    call = lambda x=FAKE, y=y, s=s, span=1, g=None, eps=1e-6, r=ctypes.byref(ok_rope), lay=None: \
+        lib.svg_qk_norm_rope(x, y, s, span, g, eps, r, lay, None)
+    assert call(x=None) == L.SVG_ERR_INVALID_ARG
+    assert call(y=FAKE) == L.SVG_ERR_INVALID_ARG                       # x and y overlap
+    assert call(y=ctypes.c_void_p((1 << 40) + 8)) == L.SVG_ERR_INVALID_ARG
+    assert call(span=3) == L.SVG_ERR_INVALID_ARG
+    assert call(eps=-1.0) == L.SVG_ERR_INVALID_ARG
+    assert call(eps=float("inf")) == L.SVG_ERR_INVALID_ARG
+    assert call(g=ctypes.c_void_p(FAKE2.value + 4)) == L.SVG_ERR_INVALID_ARG
+    assert call(s=_shape(D=80)) == L.SVG_ERR_UNSUPPORTED
+    assert call(s=_shape(H=65, D=128)) == L.SVG_ERR_UNSUPPORTED        # H*D > 8192
+    for bad in ((s.D - 62, 31, 31), (s.D, 2, 0), (-2, s.D, 2)):
+        r = L.SvgRope(*bad, 10000.0)
+        assert call(r=ctypes.byref(r)) == L.SVG_ERR_INVALID_ARG, bad
+    r = L.SvgRope(s.D - 64, 32, 32, 0.0)
+    assert call(r=ctypes.byref(r)) == L.SVG_ERR_INVALID_ARG
