@@ -106,10 +106,10 @@ def cpu_baseline(w, q, k, v, classes, budget_s):
                        f"host has {os.cpu_count()} cores")}
 
 
-def norm_rope_leg(w, s, classes, dev, stream, reps=20):
+def norm_rope_leg(w, s, classes, dev, stream, reps=50):
     """QK-Norm + 3D RoPE of one projection tensor (query or key rows) into the
-    attention input, each head in its layout, timed over `reps` calls after a
-    warm-up; beside it the same arithmetic as plain PyTorch eager ops (the
+    attention input, each head in its layout, timed over `reps` calls after ten
+    warm-up calls; beside it the same arithmetic as plain PyTorch eager ops (the
     pages' comparison point), its cos / sin table built outside the timing."""
     import torch
     import synth
@@ -122,7 +122,7 @@ def norm_rope_leg(w, s, classes, dev, stream, reps=20):
     lay = torch.from_numpy(np.tile(classes.astype(np.int32), w.B)).to(dev)
     y = svg.svg_qk_norm_rope(x, s, norm="row", gamma=gamma, rope=rope, head_layout=lay)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(3):
+    for _ in range(10):
         svg.svg_qk_norm_rope(x, s, norm="row", gamma=gamma, rope=rope, head_layout=lay, out=y)
     e0.record(stream)
     for _ in range(reps):
