@@ -18,7 +18,8 @@ import torch
 
 from .ops import (Shape, EncodedMasks, svg_build_masks, svg_encode_mask, svg_permute,
                   svg_profile_workspace_bytes, svg_profile_heads, svg_attn_workspace_bytes,
-                  svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows)
+                  svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows,
+                  svg_qk_norm_rope)
 
 
 class OnlineSparseAttention:
@@ -44,6 +45,20 @@ class OnlineSparseAttention:
             torch.empty(shape, dtype=torch.bfloat16, device=device) for _ in range(3))
         self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s), 1), dtype=torch.uint8,
                                           device=device)
+
+    def prepare_inputs(self, xq, xk, xv, norm="row", gamma_q=None, gamma_k=None, eps=1e-6, rope=None,
+                       out=None):
+        """Attention inputs from the projection rows xq, xk, xv [B, N, H, D]
+        (frame-major tokens): q and k RMS-normalised (norm = "head", "row" or
+        None, weights gamma_q / gamma_k) and turned by the 3D rotary embedding
+        rope = (d_f, d_y, d_x, theta) or not (None); v moved unchanged.  All
+        three come out frame-major [B, H, N, D] (the profiler reads every head
+        before the layouts are chosen).  out: optional (q, k, v) to fill."""
+        q, k, v = out if out is not None else (None, None, None)
+        q = svg_qk_norm_rope(xq, self.s, norm=norm, gamma=gamma_q, eps=eps, rope=rope, out=q)
+        k = svg_qk_norm_rope(xk, self.s, norm=norm, gamma=gamma_k, eps=eps, rope=rope, out=k)
+        v = svg_qk_norm_rope(xv, self.s, norm=None, rope=None, out=v)
+        return q, k, v
 
     def profile(self, q, k, v, idx):
         return svg_profile_heads(q, k, v, self.s, self.scale, idx, self.cand, self.workspace,

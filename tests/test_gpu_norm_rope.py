@@ -125,3 +125,24 @@ def test_wan_size_sampled_rows():
     rows = np.where(lay[:, None] == 1, p[toks][None, :], toks[None, :])  # [H, T]
     got = y[0][torch.arange(H)[:, None].cuda(), torch.from_numpy(rows).cuda()]
     _check(got, want, float(np.max(gamma)))
+
+
+def test_layer_prepare_inputs_then_attention():
+    """OnlineSparseAttention.prepare_inputs: q, k through norm + rotation, v
+    moved bit-exactly; the layer then runs on them like on any q, k, v."""
+    w = S.get_workload("tiny")
+    s = svg.Shape(w.B, w.H, w.N, w.D, w.F, w.Hs, w.Ws, w.block)
+    xq, xk, xv = (S.gen_projection_rows(w.B, w.N, w.H, w.D, seed=30 + i).cuda() for i in range(3))
+    gq, gk = (torch.from_numpy(S.gen_norm_weight(w.H * w.D, 40 + i)).cuda() for i in range(2))
+    rope = (24, 20, 20, 10000.0)
+    layer = svg.OnlineSparseAttention(s, w.band_w)
+    q, k, v = layer.prepare_inputs(xq, xk, xv, norm="row", gamma_q=gq, gamma_k=gk, rope=rope)
+    torch.cuda.synchronize()
+    for t, x_, g_ in ((q, xq, gq), (k, xk, gk)):
+        want = O.qk_norm_rope(x_.float().cpu().numpy(), w.F, w.Hs, w.Ws, "row", g_.cpu().numpy(), 1e-6, rope)
+        _check(t, want, float(g_.max()))
+    assert torch.equal(v, xv.transpose(1, 2).contiguous())
+    idx = torch.from_numpy(S.sample_query_idx(w)).cuda()
+    o, _ = layer(q, k, v, idx)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
