@@ -65,10 +65,17 @@ def test_small_d64(norm, use_gamma, layout):
     (48, 64, (0, 32, 32, 10000.0)),     # no frame run
     (64, 128, (128, 0, 0, 10000.0)),    # 1024 threads, frame run only
     (5, 64, (20, 22, 22, 10000.0)),     # 40 active threads in one 64-lane wave
+    (128, 64, (24, 20, 20, 10000.0)),   # H*D = 8192, the largest row: 1024 threads
 ])
 @pytest.mark.parametrize("norm", ["head", "row"])
 def test_head_counts_and_splits(H, D, rope, norm):
     y, want, gmax = _case(1, H, D, 2, 3, 8, 5, norm, True, rope, "mixed", 12)
+    _check(y, want, gmax)
+
+
+def test_three_batch_rows_per_row_layouts():
+    # B = 3: the grid's second dimension; layouts differ per (batch, head)
+    y, want, gmax = _case(3, 4, 128, 2, 3, 5, 2, "row", True, (44, 42, 42, 10000.0), "mixed", 22)
     _check(y, want, gmax)
 
 
