@@ -39,7 +39,7 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_svg_amd", "csrc", "attn.hi
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan720p",
                     choices=["tiny", "cogvideox", "wan720p", "hunyuan720p", "static_wan720p"])
@@ -69,8 +69,8 @@ def cpu_baseline(w, q, k, v, classes, budget_s):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    import synth
     if w.mode == "static":
-        import synth
         masks = {h: O.calibrate_mask(synth.energy_matrix(w, h), w.eps) for h in (0, 1)}
         jobs = [(0, 0), (1, 0)]
     else:
@@ -100,10 +100,50 @@ def cpu_baseline(w, q, k, v, classes, budget_s):
             blocks += 1
         i += 1
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle, {blocks} whole query blocks ({i} per head) of one "
-                       f"spatial and one temporal head, {flops / 1e9:.1f} GFLOP in {dt:.1f} s; "
-                       f"host has {os.cpu_count()} cores")}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": (f"fp64 NumPy oracle, {blocks} whole query blocks ({i} per head) of one "
+                      f"spatial and one temporal head, {flops / 1e9:.1f} GFLOP in {dt:.1f} s; "
+                      f"host has {os.cpu_count()} cores"),
+           "cpu_model": cpu_model(), "blas": blas_info(), "host_cores": os.cpu_count(),
+           "attention_s_per_layer_est": round(dt / max(i, 1) * w.n_blocks * w.H / len(jobs), 1)}
+    if w.mode == "online":
+        # the profiler's oracle on one head (64 samples against every key), and
+        # the permutation of one head's tensor, each scaled to the layer
+        h = jobs[0][0]
+        idx = synth.sample_query_idx(w, 0)
+        qh, kh, vh = (t[0, h:h + 1].float().numpy() for t in (q, k, v))
+        t1 = time.perf_counter()
+        O.profile_heads(qh, kh, vh, w.F, w.Hs, w.Ws, w.block, w.scale, idx, cand)
+        t_prof = time.perf_counter() - t1
+        x = k[0, h].float().numpy().astype(np.float64)
+        t1 = time.perf_counter()
+        O.to_token_major(x, w.F, w.Hs, w.Ws)
+        t_perm = time.perf_counter() - t1
+        n_t = int((classes == 1).sum())
+        out["profile"] = {"s_per_head": round(t_prof, 3), "s_per_layer": round(t_prof * w.H, 2),
+                          "note": f"oracle profile_heads on one head x {w.H} heads"}
+        out["permute"] = {"s_per_head": round(t_perm, 4), "s_per_layer": round(t_perm * n_t, 3),
+                          "note": f"oracle to_token_major of one head's K (float64) x {n_t} temporal heads"}
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        return [{"api": p.get("internal_api"), "threads": p.get("num_threads")} for p in threadpool_info()]
+    except Exception:  # pragma: no cover
+        return None
 
 
 def norm_rope_leg(w, s, classes, dev, stream, reps=50):
@@ -263,6 +303,8 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    per_med = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    step_med = float(np.median([e[0].elapsed_time(e[-1]) for e in evs]))
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -302,7 +344,11 @@ def main():
                    "layout": (("K moved by svg_permute; Q, V, O of temporal heads through the permutation "
                                "inside the attention call") if w.mode == "online" and layer.fused_layout
                               else "svg_permute of q, k, v and of op" if w.mode == "online" else "frame-major")},
+        "ms_per_step_median": round(step_med, 4),
+        "timing": f"{args.warmup} warm-up steps, then {args.steps} timed steps; HIP events on the launch "
+                  "stream around every call (mean and median over the timed steps)",
         "ms_per_call": {n: round(v, 4) for n, v in per.items()},
+        "ms_per_call_median": {n: round(v, 4) for n, v in per_med.items()},
         "attention_tflops": round(achieved, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

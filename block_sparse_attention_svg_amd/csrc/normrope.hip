@@ -152,7 +152,7 @@ __global__ __launch_bounds__(1024) void norm_rope_kernel(NormRopeArgs a) {
     g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
   }
   const int bh = b * a.H + h;
-  const bool tm = a.head_layout && a.head_layout[bh] == 1;
+  const bool tm = a.head_layout && a.head_layout[bh] != 0;
   u32x4* yh = a.y + int64_t(bh) * a.N * LPH;
 
 #pragma unroll

@@ -92,15 +92,29 @@ class OnlineSparseAttention:
 class StaticSparseAttention:
     def __init__(self, s: Shape, dense_masks: torch.Tensor, repetitive: torch.Tensor = None,
                  k_anchors: int = 5, scale: float = None):
-        """dense_masks: uint8 [H, nB, nB] (one mask per head); repetitive:
-        int32 [B*H] device flags of the row-repetitive heads (or None)."""
+        """dense_masks: uint8 [H, nB, nB] (one mask per head, shared by every
+        batch row); repetitive: int32 device flags of the row-repetitive heads,
+        [H] or [B*H] with the same flags in every batch row (the mask of a head
+        is restricted to its anchor rows once for all batch rows), or None."""
         self.s = s
         self.scale = scale if scale is not None else 1.0 / math.sqrt(s.D)
         self.k = k_anchors
-        self.repetitive = repetitive
         masks = dense_masks.clone()
+        self.repetitive = None
         if repetitive is not None:
-            svg_restrict_anchor_rows(masks, s, repetitive[: masks.shape[0]].contiguous(), k_anchors)
+            if repetitive.numel() == s.H:
+                flags = repetitive.reshape(s.H)
+            elif repetitive.numel() == s.B * s.H:
+                rows = repetitive.reshape(s.B, s.H)
+                if not torch.equal(rows, rows[:1].expand_as(rows)):
+                    raise ValueError("the masks are per head: the repetitive flags must be the same "
+                                     "in every batch row")
+                flags = rows[0]
+            else:
+                raise ValueError(f"repetitive must hold {s.H} or {s.B * s.H} flags")
+            flags = flags.contiguous()
+            svg_restrict_anchor_rows(masks, s, flags, k_anchors)
+            self.repetitive = flags.repeat(s.B).contiguous()   # per (batch, head) for the broadcast
         self.masks = svg_encode_mask(masks)
         self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s), 1), dtype=torch.uint8,
                                           device=dense_masks.device)

@@ -136,7 +136,7 @@ def svg_qk_norm_rope(x: torch.Tensor, s: Shape, norm: str = "head", gamma: torch
     normalised over each head (norm="head") or the whole row (norm="row") or
     not at all (None), turned by the 3D rotary embedding rope = (d_f, d_y, d_x,
     theta) or not (None), each head written in its layout (head_layout [B*H],
-    1 = token-major; None = all frame-major)."""
+    nonzero = token-major; None = all frame-major)."""
     if norm not in _NORM_SPAN:
         raise ValueError(f"norm must be None, 'head' or 'row' (got {norm!r})")
     if tuple(x.shape) != (s.B, s.N, s.H, s.D) or x.dtype != torch.bfloat16 or not x.is_contiguous():

@@ -133,9 +133,10 @@ typedef struct {
  *   rope       : host struct, or NULL for no rotation.  Video token
  *                n = f*Hs*Ws + yy*Ws + xx sits at (f, yy, xx); text tokens
  *                (n >= F*Hs*Ws) are not rotated.
- *   head_layout: device int32 [B*H], or NULL for all 0: heads with 1 are
- *                written token-major (video token f*S + s at row s*F + f,
- *                S = Hs*Ws), the rest frame-major.
+ *   head_layout: device int32 [B*H], or NULL for all 0: heads with a
+ *                nonzero entry are written token-major (video token f*S + s
+ *                at row s*F + f, S = Hs*Ws), the rest frame-major (the same
+ *                convention as svg_block_sparse_attn's head_layout).
  * fp32 arithmetic from the exact inputs, one rounding to bf16 (nearest even).
  * With norm_span 0 and rope NULL the call is an exact transpose / layout move
  * (V of a layer).  s.block is not read but must be valid.  x, y 16-byte

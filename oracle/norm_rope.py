@@ -82,7 +82,7 @@ def qk_norm_rope(x: np.ndarray, F: int, Hs: int, Ws: int, norm: str = "head", ga
     """[B, N, H, D] projection rows -> [B, H, N, D] attention input, fp64.
 
     norm: None, "head" or "row"; rope: None or (d_f, d_y, d_x, theta);
-    head_layout: None or int [B*H], 1 = that head's rows token-major."""
+    head_layout: None or int [B*H], nonzero = that head's rows token-major."""
     x = np.asarray(x, dtype=np.float64)
     B, N, H, D = x.shape
     y = rms_norm(x, gamma, eps, norm) if norm is not None else x.copy()
@@ -96,6 +96,6 @@ def qk_norm_rope(x: np.ndarray, F: int, Hs: int, Ws: int, norm: str = "head", ga
         lay = np.asarray(head_layout).reshape(B, H)
         for b in range(B):
             for h in range(H):
-                if lay[b, h] == 1:
+                if lay[b, h] != 0:
                     out[b, h, p, :] = y[b, h]
     return out

@@ -218,3 +218,19 @@ def test_qk_norm_rope_validation():
         assert call(r=ctypes.byref(r)) == L.SVG_ERR_INVALID_ARG, bad
     r = L.SvgRope(s.D - 64, 32, 32, 0.0)
     assert call(r=ctypes.byref(r)) == L.SVG_ERR_INVALID_ARG
+
+
+def test_static_layer_rejects_flags_that_differ_across_batch_rows():
+    """The static layer's masks are per head, shared by the batch rows: row-
+    repetitive flags that differ between batch rows are refused on the host
+    before any device call."""
+    import torch
+    from block_sparse_attention_svg_amd.layer import StaticSparseAttention
+    from block_sparse_attention_svg_amd.ops import Shape
+    s = Shape(B=2, H=3, N=256, D=64, F=1, Hs=16, Ws=16, block=128)
+    masks = torch.ones((3, 2, 2), dtype=torch.uint8)
+    flags = torch.tensor([1, 0, 0, 0, 0, 0], dtype=torch.int32)
+    with pytest.raises(ValueError, match="same in every batch row"):
+        StaticSparseAttention(s, masks, flags)
+    with pytest.raises(ValueError, match="must hold 3 or 6 flags"):
+        StaticSparseAttention(s, masks, torch.zeros(4, dtype=torch.int32))

@@ -153,3 +153,22 @@ def test_layer_prepare_inputs_then_attention():
     o, _ = layer(q, k, v, idx)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
+
+
+def test_any_nonzero_layout_is_token_major():
+    """head_layout follows the attention's convention: any nonzero entry means
+    token-major, so a layout array holding 2 or -1 gives the bits of 1."""
+    B, H, D, F, Hs, Ws, text = 1, 4, 128, 3, 6, 10, 5
+    N = F * Hs * Ws + text
+    s = svg.Shape(B=B, H=H, N=N, D=D, F=F, Hs=Hs, Ws=Ws, block=128)
+    x = S.gen_projection_rows(B, N, H, D, seed=23).cuda()
+    rope = (44, 42, 42, 10000.0)
+    odd = torch.tensor([0, 2, -1, 1], dtype=torch.int32, device="cuda")
+    ones = torch.tensor([0, 1, 1, 1], dtype=torch.int32, device="cuda")
+    y_odd = svg.svg_qk_norm_rope(x, s, norm="head", rope=rope, head_layout=odd)
+    y_one = svg.svg_qk_norm_rope(x, s, norm="head", rope=rope, head_layout=ones)
+    torch.cuda.synchronize()
+    assert torch.equal(y_odd, y_one)
+    want = O.qk_norm_rope(x.float().cpu().numpy(), F, Hs, Ws, "head", None, 1e-6, rope,
+                          odd.cpu().numpy())
+    _check(y_odd, want, 1.0)

@@ -1,8 +1,8 @@
 """GPU parity of the online head profiler.
 
 Head choice must equal the oracle's on every compared head (bit-exact); the
-reported errors must match the float64 oracle within a relative 5e-2 (the GPU
-sums bf16-rounded softmax weights in fp32).
+reported errors must match the float64 oracle within PROFILE_ERR_REL.  The
+full-size workloads (every head) are in test_gpu_full_size.py.
 """
 import numpy as np
 import pytest
@@ -11,11 +11,11 @@ import torch
 import block_sparse_attention_svg_amd as svg
 import oracle as O
 import synth as S
-from parity_utils import banner
+from parity_utils import banner, PROFILE_ERR_REL
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-ERR_REL = 5e-2
+ERR_REL = PROFILE_ERR_REL
 
 
 def shape_of(w, H=None):
@@ -36,9 +36,7 @@ def _gpu_profile(w, q, k, v, idx, cand_np=None, band_w=None):
     return choice.cpu().numpy(), err.cpu().numpy()
 
 
-@pytest.mark.parametrize("name,heads", [("tiny", None), ("cogvideox", None),
-                                        ("wan720p", [0, 1, 2, 3, 17, 39]),
-                                        ("hunyuan720p", [0, 5, 11, 23])])
+@pytest.mark.parametrize("name,heads", [("tiny", None), ("cogvideox", None)])
 def test_profile_matches_oracle(name, heads, workload_inputs):
     banner("profile", name)
     w, q, k, v, cls = workload_inputs(name, dtype="bf16")
