@@ -218,6 +218,28 @@ def norm_rope_leg(w, s, classes, dev, stream, reps=50):
                     f"rope runs {rope[:3]}, theta 1e4, temporal heads token-major; not part of the layer step"}
 
 
+def permute_leg(w, s, x, head_sel, n_temporal, stream, reps=50):
+    """svg_permute (frame-major -> token-major) of one tensor's temporal heads,
+    timed alone over `reps` calls after five warm-up calls (not part of the
+    fused layer step, where svg_prepare_kv moves K with V)."""
+    import torch
+    import block_sparse_attention_svg_amd as svg
+    y = torch.empty_like(x)
+    for _ in range(5):
+        svg.svg_permute(x, s, head_sel, out=y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        svg.svg_permute(x, s, head_sel, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    moved = 2 * n_temporal * w.N * w.D * 2
+    gbs = moved / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes": moved, "note": f"svg_permute of K, {n_temporal} temporal heads, read + write"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,7 +267,7 @@ def main():
         layer = svg.OnlineSparseAttention(s, w.band_w, scale=scale, n_samples=w.n_samples)
         n_idx = max(args.steps + args.warmup, 1)
         idx = [torch.from_numpy(synth.sample_query_idx(w, t)).to(dev) for t in range(n_idx)]
-        names = ["masks", "profile", "permute", "attention", "unpermute"]
+        names = ["masks", "profile", "layout", "attention", "unpermute"]
     else:
         E = torch.from_numpy(np.stack([synth.energy_matrix(w, h) for h in range(w.H)])).to(dev)
         dense = svg.svg_calibrate_masks(E, w.eps)
@@ -341,8 +363,10 @@ def main():
         "config": {"workload": describe(w), "heads_temporal": n_temporal,
                    "heads_spatial": w.H - n_temporal, "profiler_samples": w.n_samples,
                    "attention_gflop": round(flop / 1e9, 2),
-                   "layout": (("K moved by svg_permute; Q, V, O of temporal heads through the permutation "
-                               "inside the attention call") if w.mode == "online" and layer.fused_layout
+                   "layout": (("one svg_prepare_kv pass after the head choice (temporal heads' K token-major, "
+                               "every head's V block-transposed in its layout); Q and O of temporal heads "
+                               "through the permutation inside the attention call")
+                              if w.mode == "online" and layer.fused_layout
                               else "svg_permute of q, k, v and of op" if w.mode == "online" else "frame-major")},
         "ms_per_step_median": round(step_med, 4),
         "timing": f"{args.warmup} warm-up steps, then {args.steps} timed steps; HIP events on the launch "
@@ -356,10 +380,15 @@ def main():
     }
     if w.mode == "online":
         tensor_bytes = w.N * w.D * 2
-        n_moved = 1 if layer.fused_layout else 3             # k only when Q, V, O go through the permutation in the attention
-        moved = 2 * n_moved * n_temporal * tensor_bytes      # read + write
-        out["permute_gbs"] = round(moved / (per["permute"] * 1e-3) / 1e9, 1)
-        out["permute_hbm_frac"] = round(out["permute_gbs"] / PEAK_HBM_GBS, 4)
+        if layer.fused_layout:
+            # K of the temporal heads and V of every head, each read and written once
+            moved = 2 * (n_temporal + w.B * w.H) * tensor_bytes
+        else:
+            moved = 2 * 3 * n_temporal * tensor_bytes            # q, k, v of the temporal heads
+        out["layout_gbs"] = round(moved / (per["layout"] * 1e-3) / 1e9, 1)
+        out["layout_hbm_frac"] = round(out["layout_gbs"] / PEAK_HBM_GBS, 4)
+        out["layout_bytes"] = moved
+        out["permute"] = permute_leg(w, s, k, layer.choice, n_temporal, stream)
         kv_bytes = 2 * w.B * w.H * tensor_bytes
         out["profile_gbs"] = round(kv_bytes / (per["profile"] * 1e-3) / 1e9, 1)
         out["profile_share"] = round(per["profile"] / ms_step, 4)

@@ -48,9 +48,11 @@ _SIGS = {
     "svg_profile_workspace_bytes": (ctypes.c_size_t, [SvgShape, _I]),
     "svg_profile_heads": (_I, [_P, _P, _P, SvgShape, ctypes.c_float, _P, _I,
                                ctypes.POINTER(SvgMask), _P, _P, _P, ctypes.c_size_t, _P]),
-    "svg_block_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, SvgShape, ctypes.c_float,
+    "svg_block_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, SvgShape, ctypes.c_float,
                                    ctypes.POINTER(SvgMask), _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "svg_attn_workspace_bytes": (ctypes.c_size_t, [SvgShape]),
+    "svg_attn_workspace_bytes": (ctypes.c_size_t, [SvgShape, _I]),
+    "svg_vt_bytes": (ctypes.c_size_t, [SvgShape]),
+    "svg_prepare_kv": (_I, [_P, _P, _P, _P, SvgShape, _P, _P]),
     "svg_row_broadcast": (_I, [_P, SvgShape, _P, _I, _P]),
     "svg_restrict_anchor_rows": (_I, [_P, _I, SvgShape, _P, _I, _P]),
     "svg_calibrate_masks": (_I, [_P, _I, _I, _I, ctypes.c_double, _P, _P]),

@@ -76,7 +76,66 @@ bool overlaps(const void* a, const void* b, size_t bytes) {
   return x < y + bytes && y < x + bytes;
 }
 
+// [a, a + a_bytes) and [b, b + b_bytes) share a byte
+bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + b_bytes && y < x + a_bytes;
+}
+
 }  // namespace
+
+svg_status attn_setup(const char* fn, const void* q, const void* k, const void* v, const void* vt,
+                      void* o, const void* qp, const void* kp, const void* vp, void* op,
+                      const svg_shape& s, float scale, const svg_mask* masks,
+                      const int32_t* head_mask, const int32_t* head_layout, float* lse,
+                      AttnArgs* out) {
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (vt && s.block != 128)
+    return fail(SVG_ERR_INVALID_ARG, "%s: vt is for 128-token blocks only", fn);
+  if (!q || !k || !o || (!v && !vt)) return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / v / o", fn);
+  if (head_layout && !kp)
+    return fail(SVG_ERR_INVALID_ARG, "%s: head_layout given but kp is NULL", fn);
+  if (head_layout && s.block != 128 && (!qp || !vp || !op))
+    return fail(SVG_ERR_INVALID_ARG, "%s: 64-token blocks need all token-major twins with head_layout", fn);
+  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
+  if (svg_status st = check_mask(masks, s, fn, 0)) return st;
+  const size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
+  if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || (v && overlaps(o, v, bytes)) ||
+      (vt && overlaps(o, bytes, vt, attn_vt_bytes(s.B * s.H, s.N, s.D, s.block))))
+    return fail(SVG_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+  if (vt && (reinterpret_cast<uintptr_t>(vt) & 15))
+    return fail(SVG_ERR_INVALID_ARG, "%s: vt must be 16-byte aligned", fn);
+  if (s.block == 128 && ((n_blocks(s) + 1) / 2 > 65535 || masks->n_masks > 32768))
+    return fail(SVG_ERR_UNSUPPORTED, "%s: 128-token blocks support up to 131070 blocks and 32768 masks",
+                fn);
+  AttnArgs& a = *out;
+  a = AttnArgs{};
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.qp = qp; a.kp = kp; a.vp = vp; a.op = op;
+  a.row_ptr = masks->row_ptr;
+  a.iv = masks->iv;
+  a.n_masks = masks->n_masks;
+  a.n_qb = masks->n_qb;
+  a.n_kb = masks->n_kb;
+  a.head_mask = head_mask;
+  a.head_layout = head_layout;
+  a.lse = lse;
+  a.BH = s.B * s.H;
+  a.N = s.N; a.D = s.D; a.block = s.block;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.vt = const_cast<void*>(vt);
+  a.vt_given = vt != nullptr;
+  a.plan = nullptr;
+  a.bitmap = masks->bitmap;
+  a.F = s.F;
+  a.S = s.Hs * s.Ws;
+  a.Nv = s.F * s.Hs * s.Ws;
+  a.divF = FastDiv(uint32_t(s.F > 0 ? s.F : 1));
+  return SVG_OK;
+}
+
 }  // namespace svg
 
 using namespace svg;
@@ -227,63 +286,75 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
   return check_launch(fn);
 }
 
-svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
+svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const void* vt, void* o,
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,
                                  const int32_t* head_mask, const int32_t* head_layout, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "svg_block_sparse_attn";
-  if (svg_status st = check_shape(s, fn)) return st;
-  if (svg_status st = check_head_dim(s, fn)) return st;
-  if (!q || !k || !v || !o) return fail(SVG_ERR_INVALID_ARG, "%s: NULL q / k / v / o", fn);
-  if (head_layout && !kp)
-    return fail(SVG_ERR_INVALID_ARG, "%s: head_layout given but kp is NULL", fn);
-  if (head_layout && s.block != 128 && (!qp || !vp || !op))
-    return fail(SVG_ERR_INVALID_ARG, "%s: 64-token blocks need all token-major twins with head_layout", fn);
-  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
-  if (svg_status st = check_mask(masks, s, fn, 0)) return st;
-  size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
-  if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
-    return fail(SVG_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
-  if (s.block == 128 && ((n_blocks(s) + 1) / 2 > 65535 || masks->n_masks > 32768))
-    return fail(SVG_ERR_UNSUPPORTED, "%s: 128-token blocks support up to 131070 blocks and 32768 masks",
-                fn);
-  size_t need = attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block);
+  AttnArgs a;
+  if (svg_status st = attn_setup(fn, q, k, v, vt, o, qp, kp, vp, op, s, scale, masks, head_mask,
+                                 head_layout, lse, &a))
+    return st;
+  const size_t need = attn_workspace_bytes(a.BH, s.N, s.D, s.block, a.vt_given);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SVG_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15))
     return fail(SVG_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
-  AttnArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o;
-  a.qp = qp; a.kp = kp; a.vp = vp; a.op = op;
-  a.row_ptr = masks->row_ptr;
-  a.iv = masks->iv;
-  a.n_masks = masks->n_masks;
-  a.n_qb = masks->n_qb;
-  a.n_kb = masks->n_kb;
-  a.head_mask = head_mask;
-  a.head_layout = head_layout;
-  a.lse = lse;
-  a.BH = s.B * s.H;
-  a.N = s.N; a.D = s.D; a.block = s.block;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.vt = workspace;
-  a.plan = nullptr;
-  a.bitmap = masks->bitmap;
-  a.F = s.F;
-  a.S = s.Hs * s.Ws;
-  a.Nv = s.F * s.Hs * s.Ws;
-  a.divF = FastDiv(uint32_t(s.F > 0 ? s.F : 1));
-  if (need > 0)
+  if (need > 0) {
+    if (!a.vt_given) a.vt = workspace;
     a.plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                         (need - attn_plan_bytes(a.BH, (a.n_qb + 1) / 2)));
+  }
   launch_attn(a, as_stream(stream));
   return check_launch(fn);
 }
 
-size_t svg_attn_workspace_bytes(svg_shape s) {
+size_t svg_attn_workspace_bytes(svg_shape s, int vt_given) {
   if (check_shape(s, "svg_attn_workspace_bytes") != SVG_OK) return 0;
-  return attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block);
+  return attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block, vt_given != 0);
+}
+
+size_t svg_vt_bytes(svg_shape s) {
+  if (check_shape(s, "svg_vt_bytes") != SVG_OK) return 0;
+  return attn_vt_bytes(s.B * s.H, s.N, s.D, s.block);
+}
+
+svg_status svg_prepare_kv(const void* k, const void* v, void* kp, void* vt, svg_shape s,
+                          const int32_t* head_layout, void* stream) {
+  const char* fn = "svg_prepare_kv";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (s.block != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: V^T blocks exist for 128-token blocks only (block %d)", fn,
+                s.block);
+  if (!v || !vt) return fail(SVG_ERR_INVALID_ARG, "%s: v or vt is NULL", fn);
+  if (kp && !k) return fail(SVG_ERR_INVALID_ARG, "%s: kp given but k is NULL", fn);
+  const size_t bytes = size_t(s.B) * s.H * s.N * s.D * 2;
+  const size_t vt_bytes = attn_vt_bytes(s.B * s.H, s.N, s.D, s.block);
+  if (overlaps(vt, vt_bytes, v, bytes) || (k && overlaps(vt, vt_bytes, k, bytes)))
+    return fail(SVG_ERR_INVALID_ARG, "%s: vt overlaps an input", fn);
+  if (kp && (overlaps(kp, k, bytes) || overlaps(kp, v, bytes) || overlaps(kp, bytes, vt, vt_bytes)))
+    return fail(SVG_ERR_INVALID_ARG, "%s: kp overlaps another buffer", fn);
+  if ((reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(vt) |
+       reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(kp)) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  if ((n_blocks(s) + 1) / 2 > 65535 || int64_t(s.B) * s.H > 65535)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: up to 131070 blocks and 65535 heads", fn);
+  AttnArgs a = {};
+  a.v = v;
+  a.vp = nullptr;
+  a.head_layout = head_layout;
+  a.vt = vt;
+  a.BH = s.B * s.H;
+  a.N = s.N; a.D = s.D; a.block = s.block;
+  a.n_kb = n_blocks(s);
+  a.F = s.F;
+  a.S = s.Hs * s.Ws;
+  a.Nv = s.F * s.Hs * s.Ws;
+  a.divF = FastDiv(uint32_t(s.F));
+  launch_prepare_kv(a, k, kp, as_stream(stream));
+  return check_launch(fn);
 }
 
 svg_status svg_row_broadcast(void* o, svg_shape s, const int32_t* head_sel, int k_anchors,

@@ -975,22 +975,40 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
   }
 }
 
-// V of every head, transposed per 128-key block into the workspace
-// ([bh][kb][d][128], keys past N zero), so the attention kernel can stage V^T
-// tiles with plain 16-byte copies and read the PV operand with ds_read_b128.
-// One workgroup per (key block, head); each thread transposes 8 keys x 8 dims
-// in registers.  Heads with layout 1 read the token-major twin.
+// The layout pass of a 128-token-block attention call, one workgroup per
+// (key block, head): V of the head, transposed per 128-key block
+// ([bh][kb][d][128], keys past N zero), so the attention kernel can stage
+// V^T tiles with plain 16-byte copies and read the PV operand with
+// ds_read_b128; for a head with layout 1 the keys of a block are its
+// token-major keys (read from the token-major twin vp when given, else from v
+// through the permutation), and when kp is given the block's token-major K
+// rows are written there too ([SVG], layout transformation: the temporal
+// heads' keys made contiguous), so K and V cross HBM in one pass.  Each
+// thread transposes 8 keys x 8 dims in registers.
 template <int D>
 __global__ __launch_bounds__(256) void vt_prep_kernel(const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ vp,
                                                       const int32_t* __restrict__ head_layout,
-                                                      __bf16* __restrict__ vt, int N, int nKB,
+                                                      __bf16* __restrict__ vt, const __bf16* __restrict__ k,
+                                                      __bf16* __restrict__ kp, int N, int nKB,
                                                       AttnArgs a) {
   constexpr int BLK = 128, CPR = D / 8, TASKS = (BLK / 8) * CPR;
   const int kb = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
-  if (t >= TASKS) return;
   const bool tm = head_layout && head_layout[bh] != 0;
+  if (tm && kp) {
+    // token-major K rows of this block: row r <- frame-major row fm(r)
+    const uint4* ksrc = reinterpret_cast<const uint4*>(k + int64_t(bh) * N * D);
+    uint4* kdst = reinterpret_cast<uint4*>(kp + int64_t(bh) * N * D);
+    constexpr int PER = BLK * CPR / 256;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = t + u * 256;
+      const int r = kb * BLK + c / CPR;
+      if (r < N) kdst[int64_t(r) * CPR + c % CPR] = ksrc[int64_t(frame_major_of(r, a)) * CPR + c % CPR];
+    }
+  }
+  if (t >= TASKS) return;
   const bool gather = tm && vp == nullptr;   // token-major keys read from v through the permutation
   const uint4* src = reinterpret_cast<const uint4*>((tm && !gather ? vp : v) + int64_t(bh) * N * D);
   const int dc = t % CPR, kg = t / CPR;
@@ -1026,10 +1044,16 @@ int persistent_grid(int64_t items) {
 }
 
 template <int D>
-void launch_b128(const AttnArgs& a, hipStream_t st) {
+void launch_vt_prep(const AttnArgs& a, const void* k, void* kp, hipStream_t st) {
   hipLaunchKernelGGL((vt_prep_kernel<D>), dim3(a.n_kb, a.BH), dim3(256), 0, st,
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.vp),
-                     a.head_layout, static_cast<__bf16*>(a.vt), a.N, a.n_kb, a);
+                     a.head_layout, static_cast<__bf16*>(a.vt), static_cast<const __bf16*>(k),
+                     static_cast<__bf16*>(kp), a.N, a.n_kb, a);
+}
+
+template <int D>
+void launch_b128(const AttnArgs& a, hipStream_t st) {
+  if (!a.vt_given) launch_vt_prep<D>(a, nullptr, nullptr, st);
   const int pairs = (a.n_qb + 1) / 2;
   const int per_xcd = plan_range_cap(pairs);
   const int W = (a.n_kb + 31) / 32;
@@ -1043,10 +1067,19 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-size_t attn_workspace_bytes(int BH, int N, int D, int block) {
+size_t attn_vt_bytes(int BH, int N, int D, int block) {
+  return block == 128 ? size_t(BH) * ceil_div(N, 128) * 128 * D * 2 : 0;
+}
+
+size_t attn_workspace_bytes(int BH, int N, int D, int block, bool vt_given) {
   if (block != 128) return 0;
   const int pairs = (ceil_div(N, 128) + 1) / 2;
-  return size_t(BH) * ceil_div(N, 128) * 128 * D * 2 + attn_plan_bytes(BH, pairs);
+  return (vt_given ? 0 : attn_vt_bytes(BH, N, D, block)) + attn_plan_bytes(BH, pairs);
+}
+
+void launch_prepare_kv(const AttnArgs& a, const void* k, void* kp, hipStream_t st) {
+  if (a.D == 128) launch_vt_prep<128>(a, k, kp, st);
+  else launch_vt_prep<64>(a, k, kp, st);
 }
 
 void launch_attn(const AttnArgs& a, hipStream_t st) {

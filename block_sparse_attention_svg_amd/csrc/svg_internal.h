@@ -69,7 +69,8 @@ struct AttnArgs {
   float* lse;
   int BH, N, D, block;
   float scale_log2;  // softmax scale times log2(e)
-  void* vt;          // workspace: V of every head, block-transposed (128-key blocks)
+  void* vt;          // V of every head, block-transposed (128-key blocks)
+  bool vt_given;     // vt holds the caller's prepared V^T (else the call fills it)
   int32_t* plan;     // workspace: per head, 9 pair indices splitting its pairs over the XCDs
   const uint32_t* bitmap;  // [n_masks][n_qb][ceil(n_kb/32)]
   // token-major index t < Nv is frame-major (t % F) * S + t / F (text tokens
@@ -83,7 +84,12 @@ __device__ __forceinline__ int frame_major_of(int t, const AttnArgs& a) {
   const int s = int(a.divF.div(uint32_t(t)));
   return (t - s * a.F) * a.S + s;
 }
-size_t attn_workspace_bytes(int BH, int N, int D, int block);
+size_t attn_vt_bytes(int BH, int N, int D, int block);
+size_t attn_workspace_bytes(int BH, int N, int D, int block, bool vt_given);
+// V^T blocks of every head into a.vt (a.v, a.vp, a.head_layout, a.N, a.n_kb,
+// a.BH, a.D, the permutation fields) and, when kp is given, the token-major K
+// rows of the layout-1 heads
+void launch_prepare_kv(const AttnArgs& a, const void* k, void* kp, hipStream_t st);
 // Longest range of query-block pairs one XCD may take of a head: 1.5x the
 // even split (edge rows of banded masks carry less work), at least the even
 // split itself.
@@ -106,6 +112,13 @@ inline size_t attn_plan_bytes(int BH, int pairs) {
   return (attn_plan_work_offset(BH, pairs) + size_t(BH) * pairs) * 4;
 }
 void launch_attn(const AttnArgs& a, hipStream_t st);
+// Host-side checks of an attention call and its AttnArgs (workspace, vt and
+// plan pointers left to the caller): SVG_OK or the failing status.
+svg_status attn_setup(const char* fn, const void* q, const void* k, const void* v, const void* vt,
+                      void* o, const void* qp, const void* kp, const void* vp, void* op,
+                      const svg_shape& s, float scale, const svg_mask* masks,
+                      const int32_t* head_mask, const int32_t* head_layout, float* lse,
+                      AttnArgs* out);
 
 struct ProfileArgs {
   const void *q, *k, *v;

@@ -19,13 +19,16 @@ import torch
 from .ops import (Shape, EncodedMasks, svg_build_masks, svg_encode_mask, svg_permute,
                   svg_profile_workspace_bytes, svg_profile_heads, svg_attn_workspace_bytes,
                   svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows,
-                  svg_qk_norm_rope)
+                  svg_qk_norm_rope, svg_vt_bytes, svg_prepare_kv)
 
 
 class OnlineSparseAttention:
-    """fused_layout (128-token blocks): only K is moved to token-major order
-    by svg_permute; the attention reads the temporal heads' Q and V rows and
-    writes their O rows through the permutation, so no inverse move follows."""
+    """fused_layout (128-token blocks): after the head choice one layout pass
+    (svg_prepare_kv) writes the temporal heads' K token-major and every head's
+    V block-transposed in its layout; the attention reads the temporal heads'
+    Q rows and writes their O rows through the permutation, so no other move
+    and no inverse move follow.  Otherwise (64-token blocks) q, k, v of the
+    temporal heads go through svg_permute and op back."""
 
     def __init__(self, s: Shape, band_w: int, scale: float = None, n_samples: int = 64,
                  device="cuda", fused_layout: bool = None):
@@ -43,8 +46,10 @@ class OnlineSparseAttention:
         self.kp = torch.empty(shape, dtype=torch.bfloat16, device=device)
         self.qp, self.vp, self.op = (None, None, None) if self.fused_layout else (
             torch.empty(shape, dtype=torch.bfloat16, device=device) for _ in range(3))
-        self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s), 1), dtype=torch.uint8,
-                                          device=device)
+        self.vt = (torch.empty(svg_vt_bytes(s) // 2, dtype=torch.bfloat16, device=device)
+                   if self.fused_layout else None)
+        self.attn_workspace = torch.empty(max(svg_attn_workspace_bytes(s, self.fused_layout), 1),
+                                          dtype=torch.uint8, device=device)
 
     def prepare_inputs(self, xq, xk, xv, norm="row", gamma_q=None, gamma_k=None, eps=1e-6, rope=None,
                        out=None):
@@ -65,16 +70,19 @@ class OnlineSparseAttention:
                                  self.choice, self.err)
 
     def permute_inputs(self, q, k, v):
-        """Token-major twins of the temporal heads (K only when fused)."""
+        """The layout step after the head choice: K token-major and every
+        head's V^T blocks in one pass when fused, else svg_permute of q, k, v."""
+        if self.fused_layout:
+            svg_prepare_kv(k, v, self.s, head_layout=self.choice, kp=self.kp, vt=self.vt)
+            return
         for x, y in ((q, self.qp), (k, self.kp), (v, self.vp)):
-            if y is not None:
-                svg_permute(x, self.s, self.choice, inverse=False, out=y)
+            svg_permute(x, self.s, self.choice, inverse=False, out=y)
 
     def attend(self, q, k, v, out=None, lse=False):
         return svg_block_sparse_attn(q, k, v, self.s, self.scale, self.cand,
                                      head_mask=self.choice, head_layout=self.choice,
                                      qp=self.qp, kp=self.kp, vp=self.vp, out=out,
-                                     op=self.op, lse=lse, workspace=self.attn_workspace)
+                                     op=self.op, lse=lse, workspace=self.attn_workspace, vt=self.vt)
 
     def restore_output(self, out):
         """Frame-major output of the temporal heads (nothing to do when fused)."""

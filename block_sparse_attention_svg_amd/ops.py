@@ -190,21 +190,48 @@ def svg_profile_heads(q, k, v, s: Shape, scale: float, idx: torch.Tensor, cand: 
     return choice, err
 
 
-def svg_attn_workspace_bytes(s: Shape) -> int:
-    return int(L.lib().svg_attn_workspace_bytes(s.c()))
+def svg_attn_workspace_bytes(s: Shape, vt_given: bool = False) -> int:
+    return int(L.lib().svg_attn_workspace_bytes(s.c(), int(bool(vt_given))))
 
 
-def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
-                          head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
-                          qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False,
-                          workspace: torch.Tensor = None):
-    """Block-sparse attention; returns (o, op, lse or None).
+def svg_vt_bytes(s: Shape) -> int:
+    return int(L.lib().svg_vt_bytes(s.c()))
 
-    With head_layout, kp is required; qp, vp and op may be None (128-token
-    blocks): layout-1 heads then read Q / V from q / v and write O to `out`
-    through the permutation, and the returned op is None."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+
+def svg_prepare_kv(k, v, s: Shape, head_layout: torch.Tensor = None, kp: torch.Tensor = None,
+                   vt: torch.Tensor = None, move_k: bool = True):
+    """The layout pass of a 128-token-block layer: V of every head block-
+    transposed in its layout (vt), and K token-major for the heads with
+    head_layout != 0 (kp, when move_k).  Returns (kp or None, vt)."""
+    _need_act(v, "v", s)
+    if move_k:
+        _need_act(k, "k", s)
+        if kp is None:
+            kp = torch.empty_like(k)
+        _need_act(kp, "kp", s)
+    else:
+        kp = None
+    if vt is None:
+        vt = torch.empty(svg_vt_bytes(s) // 2, dtype=torch.bfloat16, device=v.device)
+    _need(vt, "vt", torch.bfloat16)
+    if vt.numel() * 2 < svg_vt_bytes(s):
+        raise ValueError("vt is smaller than svg_vt_bytes(s)")
+    if head_layout is not None:
+        _need(head_layout, "head_layout", torch.int32)
+    L.check("svg_prepare_kv", L.lib().svg_prepare_kv(
+        _ptr(k if move_k else None), _ptr(v), _ptr(kp), _ptr(vt), s.c(), _ptr(head_layout), _stream()))
+    return kp, vt
+
+
+def _attn_args(q, k, v, vt, s, head_mask, head_layout, qp, kp, vp, out, op, lse):
+    for t, n in ((q, "q"), (k, "k")):
         _need_act(t, n, s)
+    if v is not None or vt is None:
+        _need_act(v, "v", s)
+    if vt is not None:
+        _need(vt, "vt", torch.bfloat16)
+        if vt.numel() * 2 < svg_vt_bytes(s):
+            raise ValueError("vt is smaller than svg_vt_bytes(s)")
     if out is None:
         out = torch.empty_like(q)
     _need_act(out, "out", s)
@@ -217,13 +244,27 @@ def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
     if head_mask is not None:
         _need(head_mask, "head_mask", torch.int32)
     lse_t = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=q.device) if lse else None
-    need = svg_attn_workspace_bytes(s)
+    return out, lse_t
+
+
+def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
+                          head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
+                          qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False,
+                          workspace: torch.Tensor = None, vt: torch.Tensor = None):
+    """Block-sparse attention; returns (o, op, lse or None).
+
+    With head_layout, kp is required; qp, vp and op may be None (128-token
+    blocks): layout-1 heads then read Q / V from q / v and write O to `out`
+    through the permutation, and the returned op is None.  vt: V^T blocks
+    from svg_prepare_kv (128-token blocks; v may then be None)."""
+    out, lse_t = _attn_args(q, k, v, vt, s, head_mask, head_layout, qp, kp, vp, out, op, lse)
+    need = svg_attn_workspace_bytes(s, vt is not None)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mc = masks.c()
     L.check("svg_block_sparse_attn", L.lib().svg_block_sparse_attn(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), s.c(),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(vt), _ptr(out), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), s.c(),
         float(scale), ctypes.byref(mc), _ptr(head_mask), _ptr(head_layout), _ptr(lse_t),
         _ptr(workspace), ws_bytes, _stream()))
     return out, op, lse_t

@@ -170,12 +170,43 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
                              const svg_mask* cand, int32_t* choice, float* err,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- a4 / a6 fused: the layout pass of a 128-token-block layer ------------ */
+/* Bytes of the block-transposed V buffer of shape s (host function):
+ * B*H*ceil(N/128)*128*D*2 for 128-token blocks, 0 otherwise. */
+size_t svg_vt_bytes(svg_shape s);
+
+/* One pass over K and V after the head choice ([SVG], "Layout Transformation
+ * + Kernel": the temporal heads' tokens made contiguous in token-major
+ * order).  For every head (b, h):
+ *   vt[bh][kb][d][j] = V'[kb*128 + j][d]  (keys past N zero), where V' is the
+ *                      head's V in its layout: frame-major when
+ *                      head_layout[bh] == 0, token-major otherwise (token-major
+ *                      row t is frame-major row (t % F)*Hs*Ws + t / F, text
+ *                      rows in place);
+ *   kp[bh][t][:]     = k[bh][fm(t)][:] for heads with head_layout[bh] != 0,
+ *                      when kp is given (other heads' kp rows untouched).
+ *   k, v   : bf16 [B,H,N,D] frame-major (k may be NULL when kp is NULL).
+ *   kp     : bf16 [B,H,N,D] or NULL.
+ *   vt     : bf16, svg_vt_bytes(s) bytes, the V operand svg_block_sparse_attn
+ *            takes as `vt`.
+ *   head_layout: device int32 [B*H] or NULL (all frame-major).
+ * A pure data move: bit-exact.  128-token blocks only (SVG_ERR_UNSUPPORTED
+ * otherwise); 16-byte aligned, non-overlapping buffers. */
+svg_status svg_prepare_kv(const void* k, const void* v, void* kp, void* vt, svg_shape s,
+                          const int32_t* head_layout, void* stream);
+
 /* ---- a5: block-sparse attention ----------------------------------------- */
 /* Softmax attention restricted, per query block, to the key blocks of the
  * head's mask row ([CalibAtt] sections 2.2 and 3.3; [VDA] section 2.1 for the
  * attention itself, section 5.3 for tiled online softmax).  Only the kept
  * key blocks are read.  Not causal.
  *   q, k, v, o     : bf16 [B,H,N,D] frame-major.
+ *   vt             : the heads' V blocks as svg_prepare_kv writes them (each
+ *                    head in the layout head_layout gives it), or NULL.  With
+ *                    128-token blocks and vt given, v, vp are not read (v may
+ *                    be NULL) and the workspace holds the work plan only;
+ *                    with vt NULL the call lays V out itself, in the
+ *                    workspace.  Must be NULL for 64-token blocks.
  *   qp, kp, vp, op : bf16 [B,H,N,D] token-major twins; may be NULL when no
  *                    head uses layout 1.  With 128-token blocks only kp is
  *                    required: a layout-1 head whose qp / vp / op is NULL
@@ -194,23 +225,23 @@ svg_status svg_profile_heads(const void* q, const void* k, const void* v, svg_sh
  *                    blocks); NULL means all 0.
  *   lse            : device float [B,H,N] out (natural-log log-sum-exp of the
  *                    scaled logits, in the layout the head attends in), or NULL.
- *   workspace      : device scratch of >= svg_attn_workspace_bytes(s) bytes
- *                    (V re-laid out per key block, then a plan that splits
- *                    every head's query-block pairs over the 8 XCDs into
- *                    ranges of equal work, from the mask bitmap, and the
- *                    heads of the 8 work queues the kernel's workgroups take
- *                    those ranges from); 16-byte aligned; may be NULL when
- *                    the size is 0.  Its contents need no initialisation and
- *                    are overwritten by every call; calls in flight at the
- *                    same time need separate workspaces.
+ *   workspace      : device scratch of >= svg_attn_workspace_bytes(s, vt != NULL)
+ *                    bytes (V re-laid out per key block unless vt is given,
+ *                    then a plan that splits every head's query-block pairs
+ *                    over the 8 XCDs into ranges of equal work, from the mask
+ *                    bitmap, and the heads of the 8 work queues the kernel's
+ *                    workgroups take those ranges from); 16-byte aligned; may
+ *                    be NULL when the size is 0.  Its contents need no
+ *                    initialisation and are overwritten by every call; calls
+ *                    in flight at the same time need separate workspaces.
  * The masks' bitmap and skip list must describe the same mask (as
  * svg_encode_mask writes them): with 128-token blocks the kernel lists each
  * pair of query blocks' kept key blocks from the bitmap (and balances work
  * with it), with 64-token blocks it walks the skip list.  A query block whose mask row is empty gets o = 0
  * and lse = -inf.  bf16 inputs, fp32 accumulation and softmax, bf16 output
  * (P rounded to bf16 for the PV product; the softmax denominator sums the
- * fp32 weights). */
-svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, void* o,
+ * fp32 weights).  The result does not depend on whether vt is given. */
+svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const void* vt, void* o,
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,
                                  const int32_t* head_mask, const int32_t* head_layout,
@@ -218,11 +249,11 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, vo
                                  void* stream);
 
 /* Workspace bytes svg_block_sparse_attn needs for shape s (host function).
- * 128-token blocks: B*H*ceil(N/128)*128*D*2 (V transposed per key block), then
- * a work plan of (9*B*H + 16 rounded up to even)*4 + 8*B*H*cap*8 + B*H*pairs*4
- * bytes with pairs = ceil(ceil(N/128)/2) and cap = max(ceil(3*pairs/16),
- * ceil(pairs/8)).  64-token blocks: 0. */
-size_t svg_attn_workspace_bytes(svg_shape s);
+ * 128-token blocks: B*H*ceil(N/128)*128*D*2 (V transposed per key block; none
+ * when vt_given != 0), then a work plan of (9*B*H + 16 rounded up to
+ * even)*4 + 8*B*H*cap*8 + B*H*pairs*4 bytes with pairs = ceil(ceil(N/128)/2)
+ * and cap = max(ceil(3*pairs/16), ceil(pairs/8)).  64-token blocks: 0. */
+size_t svg_attn_workspace_bytes(svg_shape s, int vt_given);
 
 /* ---- offline calibration ([CalibAtt] section 3.1) --------------------------- */
 /* Block attention energy: energy[bh][r][c] = sum over the queries i of block r

@@ -106,40 +106,73 @@ def test_attention_validation():
     lib = L.lib()
     s = _shape()
     m = _mask(n_masks=1)
-    base = [FAKE, FAKE2, ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000),
+    # q, k, v, vt, o, qp, kp, vp, op, s, scale, masks, head_mask, head_layout, lse, ws, ws_bytes, stream
+    base = [FAKE, FAKE2, ctypes.c_void_p(0x30000000), None, ctypes.c_void_p(0x40000000),
             None, None, None, None, s, 0.125, ctypes.byref(m), None, None, None, None, 0, None]
-    a = list(base); a[12] = FAKE           # head_layout without token-major twins
+    a = list(base); a[13] = FAKE           # head_layout without token-major twins
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
-    a = list(base); a[3] = FAKE            # o aliases q
+    a = list(base); a[4] = FAKE            # o aliases q
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
-    a = list(base); a[8] = _shape(D=256)
+    a = list(base); a[9] = _shape(D=256)
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_UNSUPPORTED
     bad = _mask(n_masks=1, n=8)
-    a = list(base); a[10] = ctypes.byref(bad)
+    a = list(base); a[11] = ctypes.byref(bad)
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(base); a[3] = ctypes.c_void_p(0x60000000)   # vt with 64-token blocks
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(base); a[2] = None                           # neither v nor vt
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_INVALID_ARG
     # 128-token blocks: work items hold the pair index in 16 bits and the mask
     # index in 15, so longer rows or more masks are refused before any launch
     big = _shape(block=128, N=128 * 131072)
-    a = list(base); a[3] = ctypes.c_void_p(1 << 40); a[8] = big
-    a[10] = ctypes.byref(_mask(n_masks=1, n=131072))
+    a = list(base); a[4] = ctypes.c_void_p(1 << 40); a[9] = big
+    a[11] = ctypes.byref(_mask(n_masks=1, n=131072))
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_UNSUPPORTED
-    a = list(base); a[8] = _shape(block=128)
-    a[10] = ctypes.byref(_mask(n_masks=32769, n=8))
+    a = list(base); a[9] = _shape(block=128)
+    a[11] = ctypes.byref(_mask(n_masks=32769, n=8))
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_UNSUPPORTED
-    # 128-token blocks: V^T blocks B*H*ceil(N/128)*128*D*2 bytes, then the work
-    # plan: (9*B*H + 16 int32, rounded to even) + 8 lists of B*H*cap int32 pairs
-    # + B*H*pairs int32, cap = max(ceil(3*pairs/16), ceil(pairs/8)),
-    # pairs = ceil(ceil(N/128)/2)
+    # 128-token blocks: V^T blocks B*H*ceil(N/128)*128*D*2 bytes (none when the
+    # caller gives vt), then the work plan: (9*B*H + 16 int32, rounded to
+    # even) + 8 lists of B*H*cap int32 pairs + B*H*pairs int32,
+    # cap = max(ceil(3*pairs/16), ceil(pairs/8)), pairs = ceil(ceil(N/128)/2)
     s128 = _shape(block=128)
-    need = lib.svg_attn_workspace_bytes(s128)
+    need = lib.svg_attn_workspace_bytes(s128, 0)
     BH, pairs = 2, 4
     cap = max((3 * pairs + 15) // 16, (pairs + 7) // 8)
     plan = ((9 * BH + 16 + 1) // 2 * 2) * 4 + 8 * BH * cap * 8 + BH * pairs * 4
-    assert need == 1 * 2 * 8 * 128 * 64 * 2 + plan
-    assert lib.svg_attn_workspace_bytes(_shape()) == 0
+    vt_bytes = 1 * 2 * 8 * 128 * 64 * 2
+    assert lib.svg_vt_bytes(s128) == vt_bytes and lib.svg_vt_bytes(_shape()) == 0
+    assert need == vt_bytes + plan
+    assert lib.svg_attn_workspace_bytes(s128, 1) == plan
+    assert lib.svg_attn_workspace_bytes(_shape(), 0) == 0
     m128 = L.SvgMask(1, 8, 8, FAKE.value, FAKE.value, FAKE.value)
-    a = list(base); a[8] = s128; a[10] = ctypes.byref(m128); a[14] = ctypes.c_void_p(0x50000000); a[15] = need - 1
+    a = list(base); a[9] = s128; a[11] = ctypes.byref(m128); a[15] = ctypes.c_void_p(0x50000000); a[16] = need - 1
     assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_CAPACITY
+    a[3] = ctypes.c_void_p(0x60000000); a[16] = plan - 1   # vt given: the plan alone
+    assert lib.svg_block_sparse_attn(*a) == L.SVG_ERR_CAPACITY
+
+
+def test_prepare_kv_validation():
+    lib = L.lib()
+    s128 = _shape(block=128)
+    K, V, KP, VT = (ctypes.c_void_p(x) for x in (0x10000000, 0x20000000, 0x30000000, 0x40000000))
+    ok = [K, V, KP, VT, s128, None, None]
+    a = list(ok); a[4] = _shape()                 # 64-token blocks have no V^T blocks
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_UNSUPPORTED
+    a = list(ok); a[1] = None
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[3] = None
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[0] = None                     # kp without k
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[3] = V                        # vt aliases v
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[2] = K                        # kp aliases k
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[3] = ctypes.c_void_p(0x40000008)
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[4] = _shape(block=128, D=96)
+    assert lib.svg_prepare_kv(*a) == L.SVG_ERR_UNSUPPORTED
 
 
 def test_broadcast_calibrate_validation():

@@ -321,3 +321,61 @@ def test_fused_layout_batch2_mixed_layouts():
     torch.cuda.synchronize()
     assert torch.equal(o_t, o_f)
     assert torch.equal(lse_t, lse_f)
+
+
+def test_prepare_kv_bit_exact():
+    """svg_prepare_kv: every head's V block-transposed in its layout (keys past
+    N zero) and the layout-1 heads' K token-major, against the oracle's
+    permutation; K rows of layout-0 heads are left untouched."""
+    banner("prepare kv")
+    B, H, F, Hs, Ws, text, D = 2, 3, 5, 6, 22, 41, 128
+    N = F * Hs * Ws + text
+    g = torch.Generator().manual_seed(95)
+    k, v = (torch.randn(B, H, N, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    s = svg.Shape(B, H, N, D, F, Hs, Ws, 128)
+    nB = s.n_blocks
+    lay = torch.tensor([1, 0, 1, 0, 0, 1], dtype=torch.int32)
+    kp = torch.full((B, H, N, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    kp_out, vt = svg.svg_prepare_kv(k.to(DEV), v.to(DEV), s, head_layout=lay.to(DEV), kp=kp)
+    torch.cuda.synchronize()
+    assert kp_out is kp
+    vt = vt.view(B * H, nB, D, 128).cpu()
+    for b in range(B):
+        for h in range(H):
+            bh = b * H + h
+            kn, vn = k[b, h].float().numpy(), v[b, h].float().numpy()
+            if lay[bh]:
+                kn, vn = O.to_token_major(kn, F, Hs, Ws), O.to_token_major(vn, F, Hs, Ws)
+                assert np.array_equal(kp[b, h].float().cpu().numpy(), kn)
+            else:
+                assert torch.all(kp[b, h] == 7.0)
+            pad = np.zeros((nB * 128, D), np.float32)
+            pad[:N] = vn
+            want = pad.reshape(nB, 128, D).transpose(0, 2, 1)
+            assert np.array_equal(vt[bh].float().numpy(), want), f"vt of head {bh}"
+
+
+@pytest.mark.parametrize("layouts", [(0, 0, 0), (1, 0, 1)])
+def test_given_vt_equals_internal_layout(layouts):
+    """The attention on the caller's V^T (svg_prepare_kv) gives the bits of the
+    call that lays V out itself; v is not needed then."""
+    banner("attn vt given", layouts)
+    H, F, Hs, Ws, text, D = 3, 4, 8, 30, 19, 128
+    N = F * Hs * Ws + text
+    g = torch.Generator().manual_seed(96)
+    q, k, v = (torch.randn(1, H, N, D, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    s = svg.Shape(1, H, N, D, F, Hs, Ws, 128)
+    nB = s.n_blocks
+    rng = np.random.default_rng(97)
+    M = (rng.random((H, nB, nB)) < 0.4).astype(np.uint8)
+    M[:, :, 0] = 1
+    enc = svg.svg_encode_mask(torch.from_numpy(M).to(DEV))
+    hm = torch.arange(H, dtype=torch.int32, device=DEV)
+    lay = torch.tensor(layouts, dtype=torch.int32, device=DEV)
+    kp, vt = svg.svg_prepare_kv(k, v, s, head_layout=lay)
+    o1, _, l1 = svg.svg_block_sparse_attn(q, k, v, s, 0.1, enc, head_mask=hm, head_layout=lay, kp=kp,
+                                          lse=True)
+    o2, _, l2 = svg.svg_block_sparse_attn(q, k, None, s, 0.1, enc, head_mask=hm, head_layout=lay, kp=kp,
+                                          lse=True, vt=vt)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
