@@ -12,6 +12,7 @@ from .ops import (
     svg_block_sparse_attn, svg_row_broadcast, svg_restrict_anchor_rows, svg_calibrate_masks, svg_version,
     svg_block_energy, svg_aggregate_masks, svg_eps_schedule, svg_row_similarity,
     svg_row_similarity_workspace_bytes, svg_qk_norm_rope, svg_vt_bytes, svg_prepare_kv,
+    svg_noalloc_scratch_bytes, svg_block_sparse_attn_noalloc,
 )
 from .layer import OnlineSparseAttention, StaticSparseAttention, attention_flops, kept_pairs_per_mask
 from ._lib import SvgError, LIB_PATH
@@ -23,6 +24,7 @@ __all__ = [
     "svg_row_broadcast", "svg_restrict_anchor_rows", "svg_calibrate_masks", "svg_version",
     "svg_block_energy", "svg_aggregate_masks", "svg_eps_schedule", "svg_row_similarity",
     "svg_row_similarity_workspace_bytes", "svg_qk_norm_rope", "svg_vt_bytes", "svg_prepare_kv",
+    "svg_noalloc_scratch_bytes", "svg_block_sparse_attn_noalloc",
     "OnlineSparseAttention", "StaticSparseAttention", "attention_flops", "kept_pairs_per_mask",
     "SvgError", "LIB_PATH",
 ]

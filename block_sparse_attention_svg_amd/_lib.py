@@ -52,6 +52,9 @@ _SIGS = {
                                    ctypes.POINTER(SvgMask), _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "svg_attn_workspace_bytes": (ctypes.c_size_t, [SvgShape, _I]),
     "svg_vt_bytes": (ctypes.c_size_t, [SvgShape]),
+    "svg_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "svg_block_sparse_attn_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, SvgShape, ctypes.c_float,
+                                           ctypes.POINTER(SvgMask), _P, _P, _P, _P]),
     "svg_prepare_kv": (_I, [_P, _P, _P, _P, SvgShape, _P, _P]),
     "svg_row_broadcast": (_I, [_P, SvgShape, _P, _I, _P]),
     "svg_restrict_anchor_rows": (_I, [_P, _I, SvgShape, _P, _I, _P]),

@@ -270,6 +270,30 @@ def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
     return out, op, lse_t
 
 
+def svg_noalloc_scratch_bytes() -> int:
+    return int(L.lib().svg_noalloc_scratch_bytes())
+
+
+def svg_block_sparse_attn_noalloc(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
+                                  head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
+                                  qp=None, kp=None, vp=None, out=None, op=None, lse: bool = False,
+                                  vt: torch.Tensor = None):
+    """svg_block_sparse_attn without a workspace (the library's fixed scratch
+    array holds the work plan); 128-token blocks need vt.  Outputs must be
+    passed in (out, and lse as a tensor) by callers that cannot allocate."""
+    if isinstance(lse, torch.Tensor):
+        lse_t = lse
+        _need(lse_t, "lse", torch.float32)
+        out, _ = _attn_args(q, k, v, vt, s, head_mask, head_layout, qp, kp, vp, out, op, False)
+    else:
+        out, lse_t = _attn_args(q, k, v, vt, s, head_mask, head_layout, qp, kp, vp, out, op, lse)
+    mc = masks.c()
+    L.check("svg_block_sparse_attn_noalloc", L.lib().svg_block_sparse_attn_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(vt), _ptr(out), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), s.c(),
+        float(scale), ctypes.byref(mc), _ptr(head_mask), _ptr(head_layout), _ptr(lse_t), _stream()))
+    return out, op, lse_t
+
+
 def svg_row_broadcast(o: torch.Tensor, s: Shape, head_sel: torch.Tensor, k_anchors: int):
     _need_act(o, "o", s)
     if head_sel is not None:

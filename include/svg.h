@@ -255,6 +255,25 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, co
  * and cap = max(ceil(3*pairs/16), ceil(pairs/8)).  64-token blocks: 0. */
 size_t svg_attn_workspace_bytes(svg_shape s, int vt_given);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call and the same kernels as svg_block_sparse_attn, with the work plan of
+ * the 128-token-block kernels kept in a fixed device array of the library
+ * (svg_noalloc_scratch_bytes() = 8 MiB, one copy per GPU, held until the
+ * process ends) instead of a workspace.  With 128-token blocks vt is required
+ * (svg_prepare_kv); 64-token blocks need no scratch.  SVG_ERR_CAPACITY when
+ * the plan (svg_attn_workspace_bytes(s, 1)) exceeds the array.  No
+ * allocation of any kind.  Every call on a GPU shares that GPU's array and
+ * rewrites all of the plan it reads, so calls that overlap on one GPU (other
+ * streams, other threads) race; calls in order on one stream do not.  The
+ * results equal svg_block_sparse_attn's bit for bit. */
+size_t svg_noalloc_scratch_bytes(void);
+svg_status svg_block_sparse_attn_noalloc(const void* q, const void* k, const void* v, const void* vt,
+                                         void* o, const void* qp, const void* kp, const void* vp,
+                                         void* op, svg_shape s, float scale, const svg_mask* masks,
+                                         const int32_t* head_mask, const int32_t* head_layout,
+                                         float* lse, void* stream);
+
 /* ---- offline calibration ([CalibAtt] section 3.1) --------------------------- */
 /* Block attention energy: energy[bh][r][c] = sum over the queries i of block r
  * and the keys j of block c of the dense softmax weight exp(s_ij - lse_i),

@@ -267,3 +267,24 @@ def test_static_layer_rejects_flags_that_differ_across_batch_rows():
         StaticSparseAttention(s, masks, flags)
     with pytest.raises(ValueError, match="must hold 3 or 6 flags"):
         StaticSparseAttention(s, masks, torch.zeros(4, dtype=torch.int32))
+
+
+def test_noalloc_validation():
+    """The allocation-free attention call refuses, on the host, 128-token
+    blocks without V^T and shapes whose work plan exceeds its fixed array."""
+    lib = L.lib()
+    assert lib.svg_noalloc_scratch_bytes() == 8 << 20
+    s128 = _shape(block=128)
+    m128 = L.SvgMask(1, 8, 8, FAKE.value, FAKE.value, FAKE.value)
+    base = [FAKE, FAKE2, ctypes.c_void_p(0x30000000), None, ctypes.c_void_p(0x40000000),
+            None, None, None, None, s128, 0.125, ctypes.byref(m128), None, None, None, None]
+    assert lib.svg_block_sparse_attn_noalloc(*base) == L.SVG_ERR_INVALID_ARG
+    assert "need the caller's V^T" in _err()
+    # plan of B*H = 4096 heads x 512 pairs: about 33 MB > 8 MiB
+    big = _shape(block=128, H=4096, N=128 * 1024, F=1, Hs=1, Ws=1)
+    nb = 1024
+    mbig = L.SvgMask(1, nb, nb, FAKE.value, FAKE.value, FAKE.value)
+    a = list(base); a[3] = ctypes.c_void_p(1 << 44); a[4] = ctypes.c_void_p(1 << 45); a[9] = big
+    a[11] = ctypes.byref(mbig)
+    assert lib.svg_attn_workspace_bytes(big, 1) > lib.svg_noalloc_scratch_bytes()
+    assert lib.svg_block_sparse_attn_noalloc(*a) == L.SVG_ERR_CAPACITY
