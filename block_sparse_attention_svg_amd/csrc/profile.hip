@@ -17,7 +17,8 @@
 //   v_mfma_f32_16x16x32_bf16, the V^T operand coming from transposing LDS
 //   reads, Z_c from one more MFMA with an all-ones operand.  Each class keeps
 //   its own running max; within a 32-key step the spatial admission is the
-//   same for all keys of a query, so only two classes are live per lane.
+//   same for all keys of a query, so only two classes are live per lane, and
+//   only their MFMAs are issued (the other two are parked in registers).
 //   Writes (m_c, Z_c, U_c) per (chunk, sample, class).
 // Pass 2 (profile_merge_kernel): one workgroup per (batch*head, sample):
 //   merges the chunks in a fixed order and evaluates both errors.
@@ -78,6 +79,24 @@ __device__ __forceinline__ int token_major(int j, const Geo& g) {
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Exchange two registers of the active lanes in place (no temporary: the
+// swapped values stay in their registers, so a rarely taken swap adds no
+// register pressure to the loop around it).
+__device__ __forceinline__ void swap_lane(float& a, float& b) {
+  asm volatile("v_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_lane(f32x4& a, f32x4& b) {
+  float x[4], y[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = a[r];
+    y[r] = b[r];
+    swap_lane(x[r], y[r]);
+  }
+  a = f32x4{x[0], x[1], x[2], x[3]};
+  b = f32x4{y[0], y[1], y[2], y[3]};
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void profile_partial_kernel(ProfileArgs a, Geo g) {
@@ -174,17 +193,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  f32x4 uacc[4][C::DT];
-  f32x4 zacc[4];
+  // Per lane (its sample), the two classes of the lane's current spatial
+  // state are live: [0] kept by the temporal mask, [1] not.  The other
+  // state's two classes are parked and swapped in when the sample's spatial
+  // admission flips (at most a few key blocks per sample: its spatial band is
+  // one run of frames), so every step issues MFMAs for two classes only.
+  f32x4 uL[2][C::DT], uP[2][C::DT];
+  f32x4 zL[2], zP[2];
+  float mL[2], mP[2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    zacc[c] = f32x4{};
+  for (int c = 0; c < 2; ++c) {
+    zL[c] = f32x4{};
+    zP[c] = f32x4{};
+    mL[c] = -INFINITY;
+    mP[c] = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) uacc[c][dt] = f32x4{};
+    for (int dt = 0; dt < C::DT; ++dt) {
+      uL[c][dt] = f32x4{};
+      uP[c][dt] = f32x4{};
+    }
   }
-  float mrun[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) mrun[c] = -INFINITY;
+  bool s_live = true;   // spatial state of the live classes: S-kept (classes 0, 1) or not (2, 3)
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
@@ -238,6 +267,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
       const bool inS = (adm >> 8) & 1u;
+      // swap the parked classes in for the lanes whose spatial state flipped
+      if (__ballot(inS != s_live)) {
+        if (inS != s_live) {   // these lanes only (exec mask): exchange the register pairs in place
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int dt = 0; dt < C::DT; ++dt) swap_lane(uL[c][dt], uP[c][dt]);
+            swap_lane(zL[c], zP[c]);
+            swap_lane(mL[c], mP[c]);
+          }
+          s_live = inS;
+        }
+      }
       float x[8];
       bool inT[8];
       float m_in = -INFINITY, m_out = -INFINITY;   // this lane's max over T-kept / T-skipped keys
@@ -252,83 +294,70 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       m_in *= c2;
       m_out *= c2;
-      // the two classes live in this step: (both, S only) if inS, else (T only, none)
-      float r_in = inS ? mrun[0] : mrun[2];
-      float r_out = inS ? mrun[1] : mrun[3];
       // Fast path: no lane's block max exceeds its running max by more than
       // 2^24, so the stale maxima stay valid and no cross-lane exchange is
       // needed.  Otherwise combine the maxima over the 4 lanes of each sample
-      // and rescale the classes whose maximum moved.
-      if (__ballot(m_in > r_in + kRescaleLog2 || m_out > r_out + kRescaleLog2)) {
+      // and rescale the live classes whose maximum moved.
+      if (__ballot(m_in > mL[0] + kRescaleLog2 || m_out > mL[1] + kRescaleLog2)) {
         m_in = fmaxf(m_in, shfl_xor_f(m_in, 16));
         m_in = fmaxf(m_in, shfl_xor_f(m_in, 32));
         m_out = fmaxf(m_out, shfl_xor_f(m_out, 16));
         m_out = fmaxf(m_out, shfl_xor_f(m_out, 32));
-        const bool up_in = m_in > r_in + kRescaleLog2;
-        const bool up_out = m_out > r_out + kRescaleLog2;
-        const float al_in = up_in ? fast_exp2(r_in - m_in) : 1.f;
-        const float al_out = up_out ? fast_exp2(r_out - m_out) : 1.f;
-        float f[4];
-        f[0] = inS ? al_in : 1.f;
-        f[1] = inS ? al_out : 1.f;
-        f[2] = inS ? 1.f : al_in;
-        f[3] = inS ? 1.f : al_out;
+        const bool up_in = m_in > mL[0] + kRescaleLog2;
+        const bool up_out = m_out > mL[1] + kRescaleLog2;
+        const float f0 = up_in ? fast_exp2(mL[0] - m_in) : 1.f;
+        const float f1 = up_out ? fast_exp2(mL[1] - m_out) : 1.f;
+        zL[0] *= f0;
+        zL[1] *= f1;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          zacc[c] *= f[c];
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt) uacc[c][dt] *= f[c];
+        for (int dt = 0; dt < C::DT; ++dt) {
+          uL[0][dt] *= f0;
+          uL[1][dt] *= f1;
         }
-        if (up_in) r_in = m_in;
-        if (up_out) r_out = m_out;
-        mrun[0] = inS ? r_in : mrun[0];
-        mrun[1] = inS ? r_out : mrun[1];
-        mrun[2] = inS ? mrun[2] : r_in;
-        mrun[3] = inS ? mrun[3] : r_out;
+        if (up_in) mL[0] = m_in;
+        if (up_out) mL[1] = m_out;
       }
       bf16x8 pin, pout;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(x[i], c2, -(inT[i] ? r_in : r_out)));
+        const float p = fast_exp2(__builtin_fmaf(x[i], c2, -(inT[i] ? mL[0] : mL[1])));
         const __bf16 pb = (__bf16)p;
         pin[i] = inT[i] ? pb : (__bf16)0.0f;
         pout[i] = inT[i] ? (__bf16)0.0f : pb;
       }
-      const bf16x8 zero8 = {};
-      bf16x8 pc[4];
-      pc[0] = inS ? pin : zero8;
-      pc[1] = inS ? pout : zero8;
-      pc[2] = inS ? zero8 : pin;
-      pc[3] = inS ? zero8 : pout;
-      // ---- U_c^T += V^T P_c^T; Z_c from an all-ones operand ------------------
+      // ---- U^T += V^T P^T for the two live classes; Z from an all-ones operand
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         const char* p0 = lb + v_lane + (half * 32 * C::VROW) * 16 + dt * 32;
         bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
         bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 4 * C::VROW * 16));
         const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          uacc[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pc[c], uacc[c][dt], 0, 0, 0);
+        uL[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pin, uL[0][dt], 0, 0, 0);
+        uL[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pout, uL[1][dt], 0, 0, 0);
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        zacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[c], zacc[c], 0, 0, 0);
+      zL[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pin, zL[0], 0, 0, 0);
+      zL[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pout, zL[1], 0, 0, 0);
     }
   }
 
   // ---- write this chunk's records ---------------------------------------------
+  // classes 0, 1 (S-kept) and 2, 3 (S-skipped), each as (T-kept, T-skipped)
   float* rec = a.ws + ((int64_t(bh) * a.n_chunks + chunk) * kQ + sidx) * 4 * C::REC;
+  float* rS = rec + (s_live ? 0 : 2) * C::REC;   // the live pair's records
+  float* rP = rec + (s_live ? 2 : 0) * C::REC;   // the parked pair's records
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float* r = rec + c * C::REC;
+  for (int c = 0; c < 2; ++c) {
     if (grp == 0) {
-      r[0] = mrun[c];
-      r[1] = zacc[c][0];
+      rS[c * C::REC] = mL[c];
+      rS[c * C::REC + 1] = zL[c][0];
+      rP[c * C::REC] = mP[c];
+      rP[c * C::REC + 1] = zP[c][0];
     }
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-      *reinterpret_cast<f32x4*>(r + 4 + dt * 16 + 4 * grp) = uacc[c][dt];
+    for (int dt = 0; dt < C::DT; ++dt) {
+      *reinterpret_cast<f32x4*>(rS + c * C::REC + 4 + dt * 16 + 4 * grp) = uL[c][dt];
+      *reinterpret_cast<f32x4*>(rP + c * C::REC + 4 + dt * 16 + 4 * grp) = uP[c][dt];
+    }
   }
 }
 
