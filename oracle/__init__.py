@@ -13,6 +13,8 @@ Sources cited in the modules:
   RMSNorm: Zhang & Sennrich, "Root Mean Square Layer Normalization" (2019)
   RoPE:    Su et al., "RoFormer: Enhanced Transformer with Rotary Position
            Embedding" (2021)
+  E4M3:    Open Compute Project, "OCP 8-bit Floating Point Specification
+           (OFP8)" (2023)
 
 Every function here is pinned by a CPU test to facts other than itself; none is
 "parity unpinned".
@@ -29,6 +31,7 @@ from .calibrate import calibrate_row, calibrate_mask, block_energy, eps_schedule
 from .broadcast import row_broadcast, row_patterns, row_similarity, is_row_repetitive
 from .flops import kept_pairs, algorithmic_flops
 from .norm_rope import rms_norm, rope_angles, rope_rotate, qk_norm_rope
+from .fp8 import e4m3_value, e4m3_round, head_scale, quantize_head, vt8_key_order, vt8_blocks
 
 __all__ = [
     "token_major_index", "to_token_major", "to_frame_major",
@@ -40,4 +43,5 @@ __all__ = [
     "calibrate_row", "calibrate_mask", "block_energy", "eps_schedule", "aggregate_masks", "row_broadcast", "row_patterns", "row_similarity", "is_row_repetitive",
     "kept_pairs", "algorithmic_flops",
     "rms_norm", "rope_angles", "rope_rotate", "qk_norm_rope",
+    "e4m3_value", "e4m3_round", "head_scale", "quantize_head", "vt8_key_order", "vt8_blocks",
 ]
