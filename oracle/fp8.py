@@ -41,11 +41,12 @@ def _finite_table():
 def e4m3_round(x) -> np.ndarray:
     """E4M3 code (uint8) of the nearest representable value, ties to the even
     code (the one whose mantissa's last bit is 0); the sign bit follows x's
-    (a negative value that rounds to zero gives the negative zero code).  |x|
-    must not exceed 448 (the scaling keeps every input inside the finite
-    range)."""
+    (a negative value that rounds to zero gives the negative zero code).  A
+    value above 448 but below 464 (448 plus half its spacing of 32) is nearest
+    to 448; |x| >= 464 would overflow and is refused (the scaling keeps every
+    input below: amax * (448 / amax) exceeds 448 by an fp32 rounding at most)."""
     x = np.asarray(x, dtype=np.float64)
-    if np.any(np.abs(x) > E4M3_MAX) or np.any(np.isnan(x)):
+    if np.any(np.abs(x) >= E4M3_MAX + 16.0) or np.any(np.isnan(x)):
         raise ValueError("e4m3_round: input outside the finite E4M3 range")
     codes, vals = _finite_table()
     a = np.abs(x)

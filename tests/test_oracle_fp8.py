@@ -55,8 +55,11 @@ def test_rounding_is_nearest_against_brute_force():
     table = F8.e4m3_value(np.array([k for k in range(256) if k not in (0x7F, 0xFF)]))
     best = np.min(np.abs(x[:, None] - table[None, :]), axis=1)
     assert np.all(np.abs(F8.e4m3_value(c) - x) == best)
+    # above the largest finite value but nearer to it than to the overflow point
+    assert F8.e4m3_round(448.0 * (1 + 2.0 ** -23)) == 0x7E and F8.e4m3_round(463.9) == 0x7E
+    assert F8.e4m3_round(-449.0) == 0xFE
     with pytest.raises(ValueError):
-        F8.e4m3_round(449.0)
+        F8.e4m3_round(464.0)
 
 
 def test_head_scale_maps_amax_to_448():
@@ -71,6 +74,14 @@ def test_head_scale_maps_amax_to_448():
     assert np.all(np.abs(val - x)[big] <= 2.0 ** -4 * np.abs(x)[big] * (1 + 1e-6))
     z = F8.quantize_head(np.zeros((4, 8), np.float32))
     assert z[1] == 1.0 and z[2] == 1.0 and not z[0].any()
+
+
+def test_quantize_head_amax_product_rounding():
+    """amax * inv can exceed 448 by one fp32 rounding; it still maps to 448."""
+    for amax in (3.0, 5.1, 93.21290588, 119.2258072, 0.37):
+        x = np.array([[amax, -amax / 3, 0.0]], np.float32)
+        codes = F8.quantize_head(x)[0]
+        assert codes[0, 0] == 0x7E
 
 
 def test_vt8_layout_halves_are_contiguous_runs():
