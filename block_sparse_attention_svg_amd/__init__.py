@@ -13,6 +13,7 @@ from .ops import (
     svg_block_energy, svg_aggregate_masks, svg_eps_schedule, svg_row_similarity,
     svg_row_similarity_workspace_bytes, svg_qk_norm_rope, svg_vt_bytes, svg_prepare_kv,
     svg_noalloc_scratch_bytes, svg_block_sparse_attn_noalloc,
+    Fp8Operands, svg_fp8_vt_bytes, svg_quantize_fp8, svg_block_sparse_attn_fp8,
 )
 from .layer import OnlineSparseAttention, StaticSparseAttention, attention_flops, kept_pairs_per_mask
 from ._lib import SvgError, LIB_PATH
@@ -25,6 +26,7 @@ __all__ = [
     "svg_block_energy", "svg_aggregate_masks", "svg_eps_schedule", "svg_row_similarity",
     "svg_row_similarity_workspace_bytes", "svg_qk_norm_rope", "svg_vt_bytes", "svg_prepare_kv",
     "svg_noalloc_scratch_bytes", "svg_block_sparse_attn_noalloc",
+    "Fp8Operands", "svg_fp8_vt_bytes", "svg_quantize_fp8", "svg_block_sparse_attn_fp8",
     "OnlineSparseAttention", "StaticSparseAttention", "attention_flops", "kept_pairs_per_mask",
     "SvgError", "LIB_PATH",
 ]

@@ -53,6 +53,10 @@ _SIGS = {
     "svg_attn_workspace_bytes": (ctypes.c_size_t, [SvgShape, _I]),
     "svg_vt_bytes": (ctypes.c_size_t, [SvgShape]),
     "svg_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "svg_fp8_vt_bytes": (ctypes.c_size_t, [SvgShape]),
+    "svg_quantize_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, SvgShape, _P, _P]),
+    "svg_block_sparse_attn_fp8": (_I, [_P, _P, _P, _P, _P, SvgShape, ctypes.c_float, ctypes.POINTER(SvgMask),
+                                       _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "svg_block_sparse_attn_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, SvgShape, ctypes.c_float,
                                            ctypes.POINTER(SvgMask), _P, _P, _P, _P]),
     "svg_prepare_kv": (_I, [_P, _P, _P, _P, SvgShape, _P, _P]),

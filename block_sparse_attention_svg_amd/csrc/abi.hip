@@ -357,6 +357,104 @@ svg_status svg_prepare_kv(const void* k, const void* v, void* kp, void* vt, svg_
   return check_launch(fn);
 }
 
+size_t svg_fp8_vt_bytes(svg_shape s) {
+  if (check_shape(s, "svg_fp8_vt_bytes") != SVG_OK || s.block != 128) return 0;
+  return attn_vt_bytes(s.B * s.H, s.N, s.D, s.block) / 2;
+}
+
+svg_status svg_quantize_fp8(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8,
+                            uint8_t* vt8, float* scales, svg_shape s, const int32_t* head_layout,
+                            void* stream) {
+  const char* fn = "svg_quantize_fp8";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (s.block != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: the FP8 attention takes 128-token blocks (block %d)", fn, s.block);
+  if (!q || !k || !v || !q8 || !k8 || !vt8 || !scales)
+    return fail(SVG_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  const size_t in_bytes = size_t(s.B) * s.H * s.N * s.D * 2, codes = in_bytes / 2;
+  const size_t vt_bytes = attn_vt_bytes(s.B * s.H, s.N, s.D, s.block) / 2, sc_bytes = size_t(3) * s.B * s.H * 4;
+  const void* ins[3] = {q, k, v};
+  const void* outs[4] = {q8, k8, vt8, scales};
+  const size_t out_sz[4] = {codes, codes, vt_bytes, sc_bytes};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(outs[o], out_sz[o], ins[i], in_bytes))
+        return fail(SVG_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlaps(outs[o], out_sz[o], outs[o2], out_sz[o2]))
+        return fail(SVG_ERR_INVALID_ARG, "%s: outputs overlap", fn);
+  }
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(q8) | reinterpret_cast<uintptr_t>(k8) | reinterpret_cast<uintptr_t>(vt8) |
+       reinterpret_cast<uintptr_t>(scales)) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  AttnArgs a = {};
+  a.head_layout = head_layout;
+  a.BH = s.B * s.H;
+  a.N = s.N; a.D = s.D; a.block = s.block;
+  a.n_kb = n_blocks(s);
+  a.F = s.F;
+  a.S = s.Hs * s.Ws;
+  a.Nv = s.F * s.Hs * s.Ws;
+  a.divF = FastDiv(uint32_t(s.F));
+  launch_quantize_fp8(a, q, k, v, q8, k8, vt8, scales, as_stream(stream));
+  return check_launch(fn);
+}
+
+svg_status svg_block_sparse_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8,
+                                     const float* scales, void* o, svg_shape s, float scale,
+                                     const svg_mask* masks, const int32_t* head_mask,
+                                     const int32_t* head_layout, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const char* fn = "svg_block_sparse_attn_fp8";
+  if (svg_status st = check_shape(s, fn)) return st;
+  if (svg_status st = check_head_dim(s, fn)) return st;
+  if (s.block != 128)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: 128-token blocks only (block %d)", fn, s.block);
+  if (!q8 || !k8 || !vt8 || !scales || !o) return fail(SVG_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+  if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
+  if (svg_status st = check_mask(masks, s, fn, 0)) return st;
+  if ((n_blocks(s) + 1) / 2 > 65535 || masks->n_masks > 32768)
+    return fail(SVG_ERR_UNSUPPORTED, "%s: up to 131070 blocks and 32768 masks", fn);
+  const size_t o_bytes = size_t(s.B) * s.H * s.N * s.D * 2, codes = o_bytes / 2;
+  if (overlaps(o, o_bytes, q8, codes) || overlaps(o, o_bytes, k8, codes) ||
+      overlaps(o, o_bytes, vt8, attn_vt_bytes(s.B * s.H, s.N, s.D, s.block) / 2))
+    return fail(SVG_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+  if ((reinterpret_cast<uintptr_t>(q8) | reinterpret_cast<uintptr_t>(k8) | reinterpret_cast<uintptr_t>(vt8) |
+       reinterpret_cast<uintptr_t>(o)) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const size_t need = attn_workspace_bytes(s.B * s.H, s.N, s.D, s.block, true);
+  if (!workspace || workspace_bytes < need)
+    return fail(SVG_ERR_CAPACITY, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(SVG_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  AttnArgs a = {};
+  a.q = q8; a.k = k8; a.v = nullptr; a.o = o;
+  a.row_ptr = masks->row_ptr;
+  a.iv = masks->iv;
+  a.n_masks = masks->n_masks;
+  a.n_qb = masks->n_qb;
+  a.n_kb = masks->n_kb;
+  a.head_mask = head_mask;
+  a.head_layout = head_layout;
+  a.lse = lse;
+  a.BH = s.B * s.H;
+  a.N = s.N; a.D = s.D; a.block = s.block;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.vt = const_cast<uint8_t*>(vt8);
+  a.vt_given = true;
+  a.plan = static_cast<int32_t*>(workspace);
+  a.bitmap = masks->bitmap;
+  a.F = s.F;
+  a.S = s.Hs * s.Ws;
+  a.Nv = s.F * s.Hs * s.Ws;
+  a.divF = FastDiv(uint32_t(s.F));
+  a.f8_scales = scales;
+  launch_attn_fp8(a, as_stream(stream));
+  return check_launch(fn);
+}
+
 svg_status svg_row_broadcast(void* o, svg_shape s, const int32_t* head_sel, int k_anchors,
                              void* stream) {
   const char* fn = "svg_row_broadcast";

@@ -340,10 +340,11 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_from<0, N>(f);
 }
 
-template <int D>
+template <int D, bool F8 = false>
 struct Cfg2 {
   static constexpr int BLK = 128;
   static constexpr int WAVES = 8;
+  static constexpr int ES = F8 ? 1 : 2;   // bytes per element of the K and V^T tiles
   // LDS tiles are built from 1-KB segments, one 16-byte global->LDS wavefront
   // copy each, placed 1040 bytes apart.  A tile of R rows x W bytes has
   // NI = R W / 1024 segments; row r lives in segment r % NI at position
@@ -353,10 +354,11 @@ struct Cfg2 {
   // segment's global source is 1024/W pieces of W contiguous bytes, and a
   // lane's source offset is a per-lane constant plus s W.
   static constexpr int SEGB = 1040;
-  static constexpr int KW = D * 2, KNI = BLK * KW / 1024;   // K: 128 rows (keys) x D
-  static constexpr int VW = BLK * 2, VNI = D * VW / 1024;   // V^T: D rows x 128 keys
+  static constexpr int KW = D * ES, KNI = BLK * KW / 1024;   // K: 128 rows (keys) x D
+  static constexpr int VW = BLK * ES, VNI = D * VW / 1024;   // V^T: D rows x 128 keys
   static constexpr int KBYTES = KNI * SEGB, VBYTES = VNI * SEGB;
   static constexpr int KT = BLK / 32, DK = D / 16, DT = D / 32, PS = BLK / 16;
+  static constexpr int DK8 = D / 64, PG = BLK / 64;          // FP8: 64-deep contraction steps
   static constexpr int KPW = KNI / 4, VPW = VNI / 4;       // copies per wave of a group
   static_assert(KNI % 4 == 0 && VNI % 4 == 0, "segments split evenly over a wave group");
   // byte offset of (row, 16-byte chunk) in a tile of NI segments of W-byte rows
@@ -492,11 +494,19 @@ __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf
   }
 }
 
-// max of x over lanes l and l ^ 32 (one VALU swap of the wave halves, no LDS)
+// max of x over lanes l and l ^ 32 (one VALU swap of the wave halves, no LDS).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second: with x in both, one register ends up with the
+// lower half's values in every lane and the other with the upper half's.
+// Written in asm: through the compiler builtin the maximum of the two
+// results was folded away (only the first result was kept, so each lane got
+// the lower half's value).  The s_nops cover the VALU -> permlane and
+// permlane -> VALU operand hazards.
 __device__ __forceinline__ float max_cross_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return a;
 }
 
 // Online softmax of one 128-key block: S (raw logits) -> P (bf16), updating the
@@ -540,6 +550,130 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
       pb[s][i] = (__bf16)p;
       if (i & 1) l1 += p;
       else l0 += p;
+    }
+  }
+  l_part += l0 + l1;
+}
+
+// ---- FP8 (e4m3) products on v_mfma_f32_32x32x64_f8f6f4 --------------------
+// Operand element i (byte) of lane l covers row / column l%32 and contraction
+// index 32*(l/32) + i; the accumulator layout is that of the 32x32x16 form.
+// K rows are taken in natural order, so register r of lane l of a 32-key tile
+// holds key 8*(r/4) + 4*(l/32) + r%4.  Over the two tiles of a 64-key group
+// the 32 weights a lane holds are then exactly its P^T operand when the V^T
+// bytes of the group store keys 8a + 4h + i at position 32h + 4a + i (the
+// layout svg_quantize_fp8 writes): contraction index 32h + 16t + r is tile
+// t's register r.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // format 0 = FP8 E4M3 for both operands; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 lds_32bytes(const char* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  return i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+}
+
+// S^T (128 keys x 32 queries) = K Q^T, the operands of tile kt+1 in flight
+// while tile kt computes.
+template <int D>
+__device__ __forceinline__ void mfma_qk8(const char* kb_lds, int k_lane, const i32x8* qreg,
+                                         f32x16* sacc) {
+  using C = Cfg2<D, true>;
+  constexpr int KT_OFF = 32 / C::KNI * C::KW;   // K rows +32
+  i32x8 cur[C::DK8], nxt[C::DK8];
+#pragma unroll
+  for (int kk = 0; kk < C::DK8; ++kk) cur[kk] = lds_32bytes(kb_lds + k_lane + kk * 64);
+#pragma unroll
+  for (int kt = 0; kt < C::KT; ++kt) {
+    if (kt + 1 < C::KT) {
+#pragma unroll
+      for (int kk = 0; kk < C::DK8; ++kk)
+        nxt[kk] = lds_32bytes(kb_lds + k_lane + (kt + 1) * KT_OFF + kk * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sacc[kt] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::DK8; ++kk) sacc[kt] = mfma_f8(cur[kk], qreg[kk], sacc[kt]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < C::DK8; ++kk) cur[kk] = nxt[kk];
+  }
+}
+
+// O^T (D x 32 queries) += V^T P^T over the two 64-key groups of a block.
+template <int D>
+__device__ __forceinline__ void mfma_pv8(const char* vb_lds, int v_lane, const i32x8* pb,
+                                         f32x16* oacc) {
+  using C = Cfg2<D, true>;
+  constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
+  i32x8 cur[C::DT], nxt[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) cur[dt] = lds_32bytes(vb_lds + v_lane + dt * DT_OFF);
+#pragma unroll
+  for (int g = 0; g < C::PG; ++g) {
+    if (g + 1 < C::PG) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        nxt[dt] = lds_32bytes(vb_lds + v_lane + dt * DT_OFF + (g + 1) * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = mfma_f8(cur[dt], pb[g], oacc[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) cur[dt] = nxt[dt];
+  }
+}
+
+// Online softmax of one 128-key block for the FP8 products: as softmax_block,
+// with the weights rounded to E4M3 (nearest even) for the PV product and
+// packed in contraction order.
+template <int D>
+__device__ __forceinline__ void softmax_block8(f32x16* sacc, i32x8* pb, f32x16* oacc, float& m_run,
+                                               float& l_part, int key0, int N, int h, float c2) {
+  using C = Cfg2<D, true>;
+  if (key0 + C::BLK > N) {
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= N) sacc[kt][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+  mx = max_cross_half(mx) * c2;
+  if (mx > m_run + kRescaleLog2) {
+    const float alpha = fast_exp2(m_run - mx);
+    l_part *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+    m_run = mx;
+  }
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int g = 0; g < C::PG; ++g) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kt = 2 * g + (w >> 2), r0 = 4 * (w & 3);
+      float p[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        p[b] = fast_exp2(__builtin_fmaf(sacc[kt][r0 + b], c2, -m_run));
+        if (b & 1) l1 += p[b];
+        else l0 += p[b];
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+      pb[g][w] = word;
     }
   }
   l_part += l0 + l1;
@@ -777,6 +911,285 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   }
 }
 
+// One FP8 work item: attn_pair with E4M3 operands for both products
+// (mfma_qk8, softmax_block8, mfma_pv8), the per-head dequantization factors
+// folded into the softmax scale (q, k) and the output scale (v).  Written as
+// a function of its own so that the bf16 item keeps its register allocation.
+// The code paths shared with attn_pair keep bf16 / FP8 switches.
+// mask mask_id and, when tm, the token-major tensors.  Every thread of the
+// workgroup calls it; it synchronizes.  In its last key-block iteration
+// thread 0 takes the index of its next item from the queue head `qhead` into
+// `next_idx`, so that the atomic's round trip overlaps the item's last blocks.
+template <int D>
+__device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair, int mask_id, bool tm,
+                                             int32_t* qhead, int& next_idx) {
+  constexpr bool F8 = true;
+  using C = Cfg2<D, F8>;
+  // Separate arrays per buffer, addressed with compile-time buffer indices:
+  // the compiler can then tell that copies in flight target a buffer other
+  // than the one being read, and adds no wait for them before LDS reads.
+  __shared__ uint4 kbuf0[C::KBYTES / 16], kbuf1[C::KBYTES / 16];
+  __shared__ uint4 vbuf0[C::VBYTES / 16], vbuf1[C::VBYTES / 16];
+  char* const kb_lds[2] = {reinterpret_cast<char*>(kbuf0), reinterpret_cast<char*>(kbuf1)};
+  char* const vb_lds[2] = {reinterpret_cast<char*>(vbuf0), reinterpret_cast<char*>(vbuf1)};
+
+  // lane indices derived per item rather than kept live from one item to the next
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = wave >> 2;
+  const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);   // wave within its group
+  const int n = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int qb0 = 2 * pair;
+  const bool has_b = qb0 + 1 < a.n_qb;
+
+  const int64_t head_off = int64_t(bh) * N * D;
+  // a layout-1 head reads its Q rows from q and writes its O rows to o through
+  // the permutation when the token-major twin is not given.  FP8: q holds
+  // every head frame-major (read through the permutation), k each head in its
+  // own layout, o is frame-major.
+  const bool gq = tm && (F8 || a.qp == nullptr), so = tm && (F8 || a.op == nullptr);
+  const char* Qb = static_cast<const char*>(tm && !gq ? a.qp : a.q) + head_off * C::ES;
+  const char* Kh = static_cast<const char*>(tm && !F8 ? a.kp : a.k) + head_off * C::ES;
+  __bf16* O = static_cast<__bf16*>(tm && !so ? a.op : a.o) + head_off;
+
+  const int q_row = (qb0 + grp) * C::BLK + w4 * 32 + n;
+  // the item's block list needs its mask rows first: their words are
+  // requested ahead of the Q rows
+  const int W = (a.n_kb + 31) >> 5;
+  const uint32_t* bm0 = a.bitmap + (int64_t(mask_id) * a.n_qb + qb0) * W;
+  const uint2 words0 = seq_words(bm0, has_b, W, 0);
+  // Q as the B operand: bf16, lane holds dims 16 kk + 8 h + i; FP8, bytes
+  // 64 kk + 32 h + i
+  using QReg = std::conditional_t<F8, i32x8, bf16x8>;
+  constexpr int NQ = F8 ? C::DK8 : C::DK;
+  QReg qreg[NQ];
+  {
+    const int q_src = gq && q_row < N ? frame_major_of(q_row, a) : q_row;
+    const char* qrow = Qb + int64_t(q_src) * D * C::ES;
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk) {
+      if constexpr (F8) {
+        uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+        if (q_row < N) {
+          lo = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 32 * h);
+          hi = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 32 * h + 16);
+        }
+        qreg[kk] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      } else {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (q_row < N) u = *reinterpret_cast<const uint4*>(qrow + (16 * kk + 8 * h) * 2);
+        qreg[kk] = as_bf16x8(u);
+      }
+    }
+  }
+
+  // Copies of a group: wave w4 takes the tile's segments w4*PW .. w4*PW+PW-1.
+  // Per lane, the global source offset is lane_src + s * W for segment s.
+  const uint32_t k_lane_src = (lane / (C::KW / 16)) * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
+  const uint32_t v_lane_src = (lane / (C::VW / 16)) * C::VNI * C::VW + (lane % (C::VW / 16)) * 16;
+  const uint32_t k_w4_src = w4 * C::KPW * C::KW, v_w4_src = w4 * C::VPW * C::VW;
+  // K rows past N (ragged last block) fall outside the block's buffer range
+  // and are never fetched: their scores are masked to -inf.  A block that
+  // does not exist gets an empty range: its copies fetch nothing.
+  auto k_src = [&](int kb, bool exists) {
+    return LdsCopySrc(Kh + int64_t(exists ? kb : 0) * C::BLK * D * C::ES,
+                      exists ? min(C::BLK, N - kb * C::BLK) * D * C::ES : 0);
+  };
+  // V^T tiles come from the block-transposed workspace: [D][128] per block,
+  // keys past N already zero
+  const char* Vt = static_cast<const char*>(a.vt) + int64_t(bh) * a.n_kb * C::BLK * D * C::ES;
+  auto v_src = [&](int kb, bool exists) {
+    return LdsCopySrc(Vt + int64_t(exists ? kb : 0) * C::BLK * D * C::ES,
+                      exists ? C::BLK * D * C::ES : 0);
+  };
+  auto copy_k = [&](const LdsCopySrc& src, const char* dst) {
+    const uint32_t lds_w = lds_addr_of(dst) + w4 * C::KPW * C::SEGB;
+    static_for<C::KPW>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      src.copy16(k_lane_src, sadd<u * C::KW>(k_w4_src), sadd<u * C::SEGB>(lds_w));
+    });
+  };
+  auto copy_v = [&](const LdsCopySrc& src, const char* dst) {
+    const uint32_t lds_w = lds_addr_of(dst) + w4 * C::VPW * C::SEGB;
+    static_for<C::VPW>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      src.copy16(v_lane_src, sadd<u * C::VW>(v_w4_src), sadd<u * C::SEGB>(lds_w));
+    });
+  };
+
+  f32x16 oacc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  f32x16 sacc[C::KT];
+  using PReg = std::conditional_t<F8, i32x8, bf16x8>;
+  PReg pb[F8 ? C::PG : C::PS];
+
+  __shared__ SeqLds sl;
+  int seq_w = 0, seq_j = 1;
+  seq_scan(sl, words0, W, 0);
+  uint32_t seq_v = sl.seq[0];   // next entry, read one call ahead
+  // Next block of the merged sequence; `mine` = my row keeps it.  All waves
+  // call this at the same points, so a window refill may synchronize.
+  auto pick = [&](int& kb, bool& mine) -> bool {
+    uint32_t e = __builtin_amdgcn_readfirstlane(seq_v);
+    if ((e & 0x3fffffffu) == kSeqRefill) {
+      seq_build(sl, bm0, has_b, W, ++seq_w);
+      e = __builtin_amdgcn_readfirstlane(sl.seq[0]);
+      seq_j = 1;
+    }
+    kb = int(e & 0x3fffffffu);
+    if (kb == int(kSeqEnd)) return false;
+    seq_v = sl.seq[seq_j++];
+    mine = grp == 0 ? (e >> 30) & 1u : (e >> 31) & 1u;
+    return true;
+  };
+
+  // bf16: K row srow (+32 kt), chunk h (+2 kk); V^T row n (+32 dt), chunk h
+  // (+2 s).  FP8: K row n, chunk 2h (+4 kk); V^T row n, chunk 2h (+4 g).
+  const int srow = F8 ? n : swap_bits23(n);
+  const int k_lane = C::template at<C::KNI, C::KW>(srow, F8 ? 2 * h : h);
+  const int v_lane = C::template at<C::VNI, C::VW>(n, F8 ? 2 * h : h);
+  float c2 = a.scale_log2;
+  float o_scale = 1.f;   // FP8: V's dequantization factor
+  if constexpr (F8) {
+    c2 *= a.f8_scales[bh] * a.f8_scales[a.BH + bh];
+    o_scale = a.f8_scales[2 * a.BH + bh];
+  }
+
+  // cur: block j (K_j staged / being used); prev: block j-1 (V_{j-1})
+  int kb_cur = 0, kb_prev = 0;
+  bool mine_cur = false, mine_prev = false;
+  bool have_cur = pick(kb_cur, mine_cur);
+  bool have_prev = false;
+  if (grp == 0) copy_k(k_src(kb_cur, have_cur), kb_lds[0]);
+  __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+  barrier_lds();
+
+  auto qk = [&](const char* k_lds) {
+    if constexpr (F8) mfma_qk8<D>(k_lds, k_lane, qreg, sacc);
+    else mfma_qk<D>(k_lds, k_lane, qreg, sacc);
+  };
+  auto pv = [&](const char* v_lds) {
+    if constexpr (F8) mfma_pv8<D>(v_lds, v_lane, pb, oacc);
+    else mfma_pv<D>(v_lds, v_lane, pb, oacc);
+  };
+  auto smax = [&](int key0) {
+    if constexpr (F8) softmax_block8<D>(sacc, pb, oacc, m_run, l_part, key0, N, h, c2);
+    else softmax_block<D>(sacc, pb, oacc, m_run, l_part, key0, N, h, c2);
+  };
+
+  // Iteration j uses K buffer j%2 and V buffer (j-1)%2; unrolled by two so
+  // that every buffer is a compile-time object.
+  auto iteration = [&](auto kbuf_c) {
+    constexpr int kbuf = decltype(kbuf_c)::value;
+    const char* k_cur = kb_lds[kbuf];
+    const char* v_prev = vb_lds[kbuf ^ 1];
+    int kb_next = 0;
+    bool mine_next = false;
+    const bool have_next = have_cur && pick(kb_next, mine_next);
+    if (have_cur && !have_next && tid == 0) next_idx = atomicAdd(qhead, 1);
+
+    // ---- phase 1 --------------------------------------------------------------
+    if (grp == 0) {
+      if (have_prev && mine_prev) pv(v_prev);
+      if (have_cur && mine_cur) qk(k_cur);
+    } else {
+      if (have_prev && mine_prev) smax(kb_prev * C::BLK);
+    }
+    // No barrier between the phases: the groups share no data within an
+    // iteration (each holds its own S, P and O; the copies of this iteration
+    // refill buffers last read in the previous one), so a group that is done
+    // early starts its next phase at once.
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- phase 2 --------------------------------------------------------------
+    if (grp == 0) {
+      // K of block j+1 into the K buffer freed by block j-1, V^T of block j
+      // into the V buffer freed by block j-2
+      copy_k(k_src(kb_next, have_next), kb_lds[kbuf ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      copy_v(v_src(kb_cur, have_cur), vb_lds[kbuf]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (have_cur && mine_cur) smax(kb_cur * C::BLK);
+    } else {
+      if (have_prev && mine_prev) pv(v_prev);
+      if (have_cur && mine_cur) qk(k_cur);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+
+    kb_prev = kb_cur;
+    mine_prev = mine_cur;
+    have_prev = have_cur;
+    kb_cur = kb_next;
+    mine_cur = mine_next;
+    have_cur = have_next;
+  };
+  while (have_cur || have_prev) {
+    iteration(std::integral_constant<int, 0>{});
+    if (!(have_cur || have_prev)) break;
+    iteration(std::integral_constant<int, 1>{});
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  const float l_tot = l_part + shfl_xor_f(l_part, 32);
+  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+  {
+    // lane indices recomputed here rather than kept live through the loop
+    int tid_e = threadIdx.x;
+    asm volatile("" : "+v"(tid_e));
+    const int wave = tid_e >> 6, lane = tid_e & 63, n = lane & 31, h = lane >> 5;
+    // O goes out through LDS (the tiles are free after the loop's last
+    // barrier): each wave writes its 32 x D block row-major into its own
+    // region (rows RS bytes apart), then stores whole rows, 16 bytes per
+    // lane, instead of 16-byte pieces of 32 rows per store.
+    // (FP8 tiles are half as large: rows are not padded there but their
+    // 16-byte chunks are rotated by the row index instead)
+    constexpr int RS = F8 ? D * 2 : D * 2 + 16, LPR = D * 2 / 16, RPI = 64 / LPR;
+    static_assert(2 * 32 * RS <= C::KBYTES && C::KBYTES == C::VBYTES, "staging fits the tiles");
+    auto st_off = [&](int row, int byte) -> int {
+      if constexpr (F8) return row * RS + (((byte >> 4) ^ (row % LPR)) << 4) + (byte & 15);
+      else return row * RS + byte;
+    };
+    char* stage = ((wave >> 1) == 0 ? kb_lds[0] : (wave >> 1) == 1 ? kb_lds[1]
+                   : (wave >> 1) == 2 ? vb_lds[0] : vb_lds[1]) + (wave & 1) * 32 * RS;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = (__bf16)(oacc[dt][4 * g + j] * inv);
+        *reinterpret_cast<bf16x4*>(stage + st_off(n, (dt * 32 + 8 * g + 4 * h) * 2)) = w;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int qrow0 = (qb0 + grp) * C::BLK + w4 * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / LPR, c = lane % LPR;
+      const uint4 x = *reinterpret_cast<const uint4*>(stage + st_off(r, c * 16));
+      if (qrow0 + r < N) {
+        const int dst = so ? frame_major_of(qrow0 + r, a) : qrow0 + r;
+        *reinterpret_cast<uint4*>(O + int64_t(dst) * D + c * 8) = x;
+      }
+    }
+  }
+  if (q_row < N) {
+    if (a.lse && h == 0) {
+      const float ln2 = 0.69314718055994530942f;
+      a.lse[int64_t(bh) * N + q_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * ln2 : -INFINITY;
+    }
+  }
+}
+
 // Persistent workgroups, one per CU, take work items from eight queues, one
 // per XCD: workgroup i runs on XCD i % 8 and takes the items of that XCD's
 // work list (plan_kernel, order_kernel: the x-th of eight contiguous ranges
@@ -786,8 +1199,8 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
 // queue head.  A workgroup whose list is done takes items from the other
 // XCDs' lists.  Every item is computed the same way wherever it runs, so the
 // result does not depend on the schedule.
-template <int D>
-__global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap) {
+template <int D, bool F8>
+__device__ __forceinline__ void persistent_items(const AttnArgs& a, int cap) {
   const int xcd = blockIdx.x % 8;
   const int32_t* counts = a.plan + a.BH * 9;
   int32_t* heads = a.plan + a.BH * 9 + 8;
@@ -814,12 +1227,26 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap)
     const int ix = __builtin_amdgcn_readfirstlane(grabbed.x);
     const int iy = __builtin_amdgcn_readfirstlane(grabbed.y);
     if (iy < 0) break;
-    attn_pair<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
+    if constexpr (F8)
+      attn_pair_f8<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
+    else
+      attn_pair<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
     // attn_pair ends with no barrier: the next take must not overwrite
     // `grabbed` before every wave has read it, nor the next item's copies
     // land in tiles a slow wave still reads for its output
     __syncthreads();
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap) {
+  persistent_items<D, false>(a, cap);
+}
+
+// The same schedule with FP8 (E4M3) operands for both products.
+template <int D>
+__global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(AttnArgs a, int cap) {
+  persistent_items<D, true>(a, cap);
 }
 
 // Work of query-block pair p of a mask: key blocks in the union of its two
@@ -1051,9 +1478,9 @@ void launch_vt_prep(const AttnArgs& a, const void* k, void* kp, hipStream_t st) 
                      static_cast<__bf16*>(kp), a.N, a.n_kb, a);
 }
 
-template <int D>
+template <int D, bool F8>
 void launch_b128(const AttnArgs& a, hipStream_t st) {
-  if (!a.vt_given) launch_vt_prep<D>(a, nullptr, nullptr, st);
+  if (!F8 && !a.vt_given) launch_vt_prep<D>(a, nullptr, nullptr, st);
   const int pairs = (a.n_qb + 1) / 2;
   const int per_xcd = plan_range_cap(pairs);
   const int W = (a.n_kb + 31) / 32;
@@ -1061,8 +1488,9 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
                      a.n_qb, W, pairs, per_xcd, a.plan);
   hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.head_mask, a.head_layout, a.n_masks,
                      a.n_kb, a.BH, pairs, a.BH * per_xcd, a.plan);
-  hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), dim3(persistent_grid(int64_t(a.BH) * pairs)),
-                     dim3(512), 0, st, a, a.BH * per_xcd);
+  const dim3 grid(persistent_grid(int64_t(a.BH) * pairs));
+  if constexpr (F8) hipLaunchKernelGGL((attn_fwd_fp8_kernel<D>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  else hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
 }
 
 }  // namespace
@@ -1084,12 +1512,17 @@ void launch_prepare_kv(const AttnArgs& a, const void* k, void* kp, hipStream_t s
 
 void launch_attn(const AttnArgs& a, hipStream_t st) {
   if (a.block == 128) {
-    if (a.D == 128) launch_b128<128>(a, st);
-    else launch_b128<64>(a, st);
+    if (a.D == 128) launch_b128<128, false>(a, st);
+    else launch_b128<64, false>(a, st);
   } else {
     if (a.D == 128) launch_t<128, 64>(a, st);
     else launch_t<64, 64>(a, st);
   }
+}
+
+void launch_attn_fp8(const AttnArgs& a, hipStream_t st) {
+  if (a.D == 128) launch_b128<128, true>(a, st);
+  else launch_b128<64, true>(a, st);
 }
 
 }  // namespace svg

@@ -1,0 +1,157 @@
+// FP8 (E4M3) operands for the FP8 attention variant ([CalibAtt] section 3.3:
+// mixed precision with FP8 on the critical path).  One scale per (tensor,
+// head): amax = max |x| over the head, every element multiplied by
+// 448 / amax in fp32 and rounded to E4M3 (nearest even, v_cvt_pk_fp8_f32),
+// the dequantization factor amax / 448 kept for the attention.  The codes go
+// straight into the layouts the FP8 attention reads: Q rows frame-major, K
+// rows in each head's layout, V block-transposed per 128 keys in each head's
+// layout with the keys of every 64-key group ordered for the 64-deep FP8
+// product (keys 8a + 4h + i at byte 32h + 4a + i).
+#include "svg_internal.h"
+
+namespace svg {
+namespace {
+
+__global__ void fp8_zero_kernel(uint32_t* amax, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) amax[i] = 0u;
+}
+
+// max |x| of one (tensor, head): blockIdx.y = head, blockIdx.z = tensor
+// (q, k, v); the float bits of non-negative values order like the values, so
+// an unsigned atomic max combines the workgroups.
+__global__ __launch_bounds__(256) void fp8_amax_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
+                                                       const uint4* __restrict__ v, int64_t chunks_per_head,
+                                                       uint32_t* __restrict__ amax, int BH) {
+  const int bh = blockIdx.y, t = blockIdx.z;
+  const uint4* x = (t == 0 ? q : t == 1 ? k : v) + int64_t(bh) * chunks_per_head;
+  uint32_t m = 0u;
+  for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < chunks_per_head; c += int64_t(gridDim.x) * 256) {
+    const uint4 u = x[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // |bf16| bits widened to fp32 bits: the order of the values is kept
+      m = max(m, (w[j] & 0x7fffu) << 16);
+      m = max(m, w[j] & 0x7fff0000u);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), off, 64)));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(amax + t * BH + bh, m);
+}
+
+__device__ __forceinline__ float inv_scale(uint32_t amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a > 0.f ? __fdiv_rn(448.f, a) : 1.f;
+}
+
+// 8 bf16 (a 16-byte chunk) times inv, rounded to E4M3: 8 bytes
+__device__ __forceinline__ uint2 to_e4m3(uint4 u, float inv) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __fmul_rn(__uint_as_float(w[j] << 16), inv);
+    f[2 * j + 1] = __fmul_rn(__uint_as_float(w[j] & 0xffff0000u), inv);
+  }
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return make_uint2(uint32_t(lo), uint32_t(hi));
+}
+
+// One workgroup per (128-token block, head): Q rows, K rows (in the head's
+// layout) and the V^T block (in the head's layout) of that block.
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                        const __bf16* __restrict__ v, uint8_t* __restrict__ q8,
+                                                        uint8_t* __restrict__ k8, uint8_t* __restrict__ vt8,
+                                                        const uint32_t* __restrict__ amax,
+                                                        const int32_t* __restrict__ head_layout, AttnArgs a) {
+  constexpr int BLK = 128, CPR = D / 8;
+  const int kb = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int N = a.N, BH = a.BH;
+  const bool tm = head_layout && head_layout[bh] != 0;
+  const float iq = inv_scale(amax[bh]), ik = inv_scale(amax[BH + bh]), iv = inv_scale(amax[2 * BH + bh]);
+  const int64_t off = int64_t(bh) * N * D;
+  const uint4* qs = reinterpret_cast<const uint4*>(q + off);
+  const uint4* ks = reinterpret_cast<const uint4*>(k + off);
+  const uint4* vs = reinterpret_cast<const uint4*>(v + off);
+  uint2* qd = reinterpret_cast<uint2*>(q8 + off);
+  uint2* kd = reinterpret_cast<uint2*>(k8 + off);
+  // Q rows (frame-major) and K rows (row r of the head's layout <- k[fm(r)])
+#pragma unroll
+  for (int u = 0; u < BLK * CPR / 256; ++u) {
+    const int c = t + u * 256;
+    const int r = kb * BLK + c / CPR, col = c % CPR;
+    if (r < N) {
+      qd[int64_t(r) * CPR + col] = to_e4m3(qs[int64_t(r) * CPR + col], iq);
+      const int src = tm ? frame_major_of(r, a) : r;
+      kd[int64_t(r) * CPR + col] = to_e4m3(ks[int64_t(src) * CPR + col], ik);
+    }
+  }
+  // V^T: thread (kg, dc) takes keys 8 kg .. 8 kg + 7 and dims 8 dc .. 8 dc + 7
+  constexpr int TASKS = (BLK / 8) * CPR;
+  if (t >= TASKS) return;
+  const int dc = t % CPR, kg = t / CPR;
+  uint2 rows[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = kb * BLK + 8 * kg + i;
+    const int src = tm && key < N ? frame_major_of(key, a) : key;
+    rows[i] = key < N ? to_e4m3(vs[int64_t(src) * CPR + dc], iv) : make_uint2(0u, 0u);
+  }
+  // byte j of rows[i] is (key 8 kg + i, dim 8 dc + j); keys i = 0..3 go to
+  // bytes 64 g + 4 (kg % 8) + i of the V^T row, keys 4..7 32 bytes further
+  uint8_t* blk = vt8 + (int64_t(bh) * a.n_kb + kb) * BLK * D;
+  const int pos0 = 64 * (kg / 8) + 4 * (kg % 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b0 = ((j < 4 ? rows[i].x : rows[i].y) >> (8 * (j & 3))) & 0xffu;
+      const uint32_t b1 = ((j < 4 ? rows[i + 4].x : rows[i + 4].y) >> (8 * (j & 3))) & 0xffu;
+      lo |= b0 << (8 * i);
+      hi |= b1 << (8 * i);
+    }
+    uint8_t* row = blk + (8 * dc + j) * BLK;
+    *reinterpret_cast<uint32_t*>(row + pos0) = lo;
+    *reinterpret_cast<uint32_t*>(row + pos0 + 32) = hi;
+  }
+}
+
+__global__ void fp8_finalize_kernel(uint32_t* scales, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float a = __uint_as_float(scales[i]);
+    scales[i] = __float_as_uint(a > 0.f ? __fdiv_rn(a, 448.f) : 1.f);
+  }
+}
+
+}  // namespace
+
+void launch_quantize_fp8(const AttnArgs& a, const void* q, const void* k, const void* v, uint8_t* q8,
+                         uint8_t* k8, uint8_t* vt8, float* scales, hipStream_t st) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(scales);
+  const int n = 3 * a.BH;
+  hipLaunchKernelGGL(fp8_zero_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, bits, n);
+  const int64_t chunks = int64_t(a.N) * a.D / 8;
+  const int per_head = int(std::min<int64_t>(64, (chunks + 256 * 16 - 1) / (256 * 16)));
+  hipLaunchKernelGGL(fp8_amax_kernel, dim3(per_head, a.BH, 3), dim3(256), 0, st,
+                     static_cast<const uint4*>(q), static_cast<const uint4*>(k), static_cast<const uint4*>(v),
+                     chunks, bits, a.BH);
+  if (a.D == 128)
+    hipLaunchKernelGGL(fp8_quant_kernel<128>, dim3(a.n_kb, a.BH), dim3(256), 0, st,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), q8, k8, vt8, bits, a.head_layout, a);
+  else
+    hipLaunchKernelGGL(fp8_quant_kernel<64>, dim3(a.n_kb, a.BH), dim3(256), 0, st,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), q8, k8, vt8, bits, a.head_layout, a);
+  hipLaunchKernelGGL(fp8_finalize_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, bits, n);
+}
+
+}  // namespace svg

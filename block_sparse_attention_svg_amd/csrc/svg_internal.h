@@ -77,6 +77,9 @@ struct AttnArgs {
   // keep their index): used for layout-1 heads whose twin qp / vp / op is NULL
   int F, S, Nv;
   FastDiv divF;
+  // FP8 calls: dequantization factors, [3][BH] (q, k, v); q, k and vt then
+  // hold E4M3 codes
+  const float* f8_scales;
 };
 // frame-major index of token-major index t
 __device__ __forceinline__ int frame_major_of(int t, const AttnArgs& a) {
@@ -112,6 +115,14 @@ inline size_t attn_plan_bytes(int BH, int pairs) {
   return (attn_plan_work_offset(BH, pairs) + size_t(BH) * pairs) * 4;
 }
 void launch_attn(const AttnArgs& a, hipStream_t st);
+// FP8 attention (128-token blocks): a.q E4M3 codes frame-major, a.k each head
+// in its layout, a.vt the V^T blocks of svg_quantize_fp8, a.f8_scales set
+void launch_attn_fp8(const AttnArgs& a, hipStream_t st);
+// E4M3 codes of q, k, v in the FP8 attention's layouts and the [3][BH]
+// dequantization factors (a.N, a.D, a.BH, a.n_kb, a.head_layout and the
+// permutation fields set)
+void launch_quantize_fp8(const AttnArgs& a, const void* q, const void* k, const void* v, uint8_t* q8,
+                         uint8_t* k8, uint8_t* vt8, float* scales, hipStream_t st);
 // Host-side checks of an attention call and its AttnArgs (workspace, vt and
 // plan pointers left to the caller): SVG_OK or the failing status.
 svg_status attn_setup(const char* fn, const void* q, const void* k, const void* v, const void* vt,

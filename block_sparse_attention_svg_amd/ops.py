@@ -270,6 +270,64 @@ def svg_block_sparse_attn(q, k, v, s: Shape, scale: float, masks: EncodedMasks,
     return out, op, lse_t
 
 
+def svg_fp8_vt_bytes(s: Shape) -> int:
+    return int(L.lib().svg_fp8_vt_bytes(s.c()))
+
+
+@dataclass
+class Fp8Operands:
+    """E4M3 codes of q, k, v in the FP8 attention's layouts and their [3, B*H]
+    dequantization factors (svg_quantize_fp8)."""
+    q8: torch.Tensor       # uint8 [B, H, N, D], frame-major
+    k8: torch.Tensor       # uint8 [B, H, N, D], each head in its layout
+    vt8: torch.Tensor      # uint8 [svg_fp8_vt_bytes]
+    scales: torch.Tensor   # float32 [3, B*H]
+
+
+def svg_quantize_fp8(q, k, v, s: Shape, head_layout: torch.Tensor = None, out: Fp8Operands = None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need_act(t, n, s)
+    if head_layout is not None:
+        _need(head_layout, "head_layout", torch.int32)
+    if out is None:
+        dev = q.device
+        shape = (s.B, s.H, s.N, s.D)
+        out = Fp8Operands(torch.empty(shape, dtype=torch.uint8, device=dev),
+                          torch.empty(shape, dtype=torch.uint8, device=dev),
+                          torch.empty(svg_fp8_vt_bytes(s), dtype=torch.uint8, device=dev),
+                          torch.empty((3, s.B * s.H), dtype=torch.float32, device=dev))
+    for t, n in ((out.q8, "q8"), (out.k8, "k8"), (out.vt8, "vt8")):
+        _need(t, n, torch.uint8)
+    _need(out.scales, "scales", torch.float32)
+    L.check("svg_quantize_fp8", L.lib().svg_quantize_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out.q8), _ptr(out.k8), _ptr(out.vt8), _ptr(out.scales), s.c(),
+        _ptr(head_layout), _stream()))
+    return out
+
+
+def svg_block_sparse_attn_fp8(ops8: Fp8Operands, s: Shape, scale: float, masks: EncodedMasks,
+                              head_mask: torch.Tensor = None, head_layout: torch.Tensor = None,
+                              out: torch.Tensor = None, lse: bool = False, workspace: torch.Tensor = None):
+    """FP8 block-sparse attention; returns (o bf16 [B,H,N,D] frame-major, lse or None)."""
+    dev = ops8.q8.device
+    if out is None:
+        out = torch.empty((s.B, s.H, s.N, s.D), dtype=torch.bfloat16, device=dev)
+    _need_act(out, "out", s)
+    for t, n in ((head_mask, "head_mask"), (head_layout, "head_layout")):
+        if t is not None:
+            _need(t, n, torch.int32)
+    lse_t = torch.empty((s.B, s.H, s.N), dtype=torch.float32, device=dev) if lse else None
+    need = svg_attn_workspace_bytes(s, True)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    mc = masks.c()
+    L.check("svg_block_sparse_attn_fp8", L.lib().svg_block_sparse_attn_fp8(
+        _ptr(ops8.q8), _ptr(ops8.k8), _ptr(ops8.vt8), _ptr(ops8.scales), _ptr(out), s.c(), float(scale),
+        ctypes.byref(mc), _ptr(head_mask), _ptr(head_layout), _ptr(lse_t), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out, lse_t
+
+
 def svg_noalloc_scratch_bytes() -> int:
     return int(L.lib().svg_noalloc_scratch_bytes())
 

@@ -255,6 +255,47 @@ svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, co
  * and cap = max(ceil(3*pairs/16), ceil(pairs/8)).  64-token blocks: 0. */
 size_t svg_attn_workspace_bytes(svg_shape s, int vt_given);
 
+/* ---- FP8 variant ([CalibAtt] section 3.3: FP8 on the critical path) -------- */
+/* Bytes of the FP8 V^T block buffer: B*H*ceil(N/128)*128*D for 128-token
+ * blocks, 0 otherwise (host function). */
+size_t svg_fp8_vt_bytes(svg_shape s);
+
+/* E4M3 operands of the FP8 attention, one scale per (tensor, head).  For
+ * x in {q, k, v} of head (b, h): amax = max |x|, inv = 448 / amax in fp32 (1
+ * when amax = 0); every element is multiplied by inv in fp32 and rounded to
+ * OCP E4M3 (nearest, ties to even; largest finite value 448).
+ *   q, k, v : bf16 [B,H,N,D] frame-major.
+ *   q8      : uint8 [B,H,N,D], every head frame-major.
+ *   k8      : uint8 [B,H,N,D], each head in its layout (head_layout != 0:
+ *             token-major rows, token-major row t = frame-major row
+ *             (t % F)*Hs*Ws + t / F, text rows in place).
+ *   vt8     : uint8, svg_fp8_vt_bytes(s): per head and 128-key block (keys
+ *             in the head's layout) a [D][128] byte tile whose keys
+ *             8a + 4h + i of each 64-key group sit at byte 32h + 4a + i;
+ *             keys past N are 0.
+ *   scales  : device float [3][B*H] out: the dequantization factors
+ *             amax / 448 (1 when amax = 0) of q, k and v.
+ *   head_layout: device int32 [B*H] or NULL (all frame-major).
+ * 128-token blocks, D in {64, 128}; 16-byte aligned, non-overlapping. */
+svg_status svg_quantize_fp8(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8,
+                            uint8_t* vt8, float* scales, svg_shape s, const int32_t* head_layout,
+                            void* stream);
+
+/* Block-sparse attention with both products on FP8 (E4M3) operands
+ * (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation): S = scale * d_q * d_k *
+ * (q8 . k8), the online softmax in fp32, P rounded to E4M3 for the PV
+ * product, O = d_v * sum(P v8) / sum(P) with the denominator in fp32, output
+ * bf16 [B,H,N,D] frame-major for every head (layout-1 heads read their Q rows
+ * and write their O rows through the permutation).  q8, k8, vt8, scales as
+ * svg_quantize_fp8 writes them for the same head_layout; masks, head_mask,
+ * head_layout, lse as for svg_block_sparse_attn.  workspace: the work plan,
+ * >= svg_attn_workspace_bytes(s, 1) bytes.  128-token blocks only. */
+svg_status svg_block_sparse_attn_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* vt8,
+                                     const float* scales, void* o, svg_shape s, float scale,
+                                     const svg_mask* masks, const int32_t* head_mask,
+                                     const int32_t* head_layout, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * call and the same kernels as svg_block_sparse_attn, with the work plan of

@@ -55,3 +55,49 @@ def sample_qblocks(n_blocks: int, seed: int, n: int = 32, must=()):
     k = max(0, min(len(rest), n - len(fixed)))
     pick = np.random.default_rng(seed).choice(rest, size=k, replace=False) if k else []
     return sorted(set(fixed) | set(int(b) for b in pick))
+
+
+# FP8 variant.  The oracle takes the E4M3-rounded q, k, v (oracle.fp8); what
+# remains on the GPU side is (i) the FP8 product's internal accumulation,
+# measured on v_mfma_f32_32x32x64_f8f6f4 at 1.5e-4 of sum |a_i b_i| and
+# bounded here by 2^-11, which moves every score by at most
+# E = 2^-11 * scale * d_q d_k * sum_d |q8_d k8_d|, (ii) the weights rounded to
+# E4M3 for the PV product (|dw| <= 2^-4 w in the normal range, <= min(w, 2^-10)
+# below it, w relative to the row's max, whatever power of two the kernel's
+# running max puts on them), (iii) bf16 rounding of the output and fp32 sums.
+FP8_MMA_REL = 2.0 ** -11
+
+
+def fp8_bound(qd, kd, vd, M, B, scale, qblocks):
+    """Per-element bound on |o_fp8 - o| and per-row bound on |lse_fp8 - lse| of
+    one head (float64 [N, D] and [N]; NaN outside qblocks), o and lse being
+    the oracle's attention on the dequantized q, k, v in the mask's layout."""
+    N, D = qd.shape
+    bnd = np.full((N, D), np.nan)
+    e_lse = np.full(N, np.nan)
+    q_abs, k_abs = np.abs(qd), np.abs(kd)
+    for r in qblocks:
+        rows = slice(r * B, min(N, (r + 1) * B))
+        kept = np.nonzero(M[r])[0]
+        if kept.size == 0:
+            bnd[rows] = 1e-6
+            e_lse[rows] = 0.0
+            continue
+        keys = np.concatenate([np.arange(c * B, min(N, (c + 1) * B)) for c in kept])
+        s = (qd[rows] @ kd[keys].T) * scale
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)
+        z = w.sum(axis=1, keepdims=True)
+        v = vd[keys]
+        oo = (w @ v) / z
+        # score error: the FP8 product's accumulation plus the fp32 scale factors
+        E = (FP8_MMA_REL * scale * (q_abs[rows] @ k_abs[keys].T).max(axis=1, keepdims=True)
+             + 2.0 ** -20 * np.abs(s).max(axis=1, keepdims=True))
+        dw = np.where(w >= 2.0 ** -6, 2.0 ** -4 * w, np.maximum(2.0 ** -4 * w, np.minimum(w, 2.0 ** -10)))
+        t_p = (dw @ np.abs(v)) / z
+        # sum_j w_j |v_jd - o_d| / z <= sum_j w_j |v_jd| / z + |o_d|
+        spread = (w @ np.abs(v)) / z + np.abs(oo)
+        t_s = (np.exp(E) - 1.0) * np.exp(E) * spread
+        bnd[rows] = t_p + t_s + 2.0 ** -8 * np.abs(oo) + 1e-3
+        e_lse[rows] = E[:, 0] + 1e-3
+    return bnd, e_lse

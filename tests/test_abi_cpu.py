@@ -288,3 +288,32 @@ def test_noalloc_validation():
     a[11] = ctypes.byref(mbig)
     assert lib.svg_attn_workspace_bytes(big, 1) > lib.svg_noalloc_scratch_bytes()
     assert lib.svg_block_sparse_attn_noalloc(*a) == L.SVG_ERR_CAPACITY
+
+
+def test_fp8_validation():
+    lib = L.lib()
+    s128 = _shape(block=128)
+    assert lib.svg_fp8_vt_bytes(s128) == 1 * 2 * 8 * 128 * 64 and lib.svg_fp8_vt_bytes(_shape()) == 0
+    bufs = [ctypes.c_void_p(x << 24) for x in range(1, 8)]
+    q, k, v, q8, k8, vt8, sc = bufs
+    ok = [q, k, v, q8, k8, vt8, sc, s128, None, None]
+    a = list(ok); a[7] = _shape()
+    assert lib.svg_quantize_fp8(*a) == L.SVG_ERR_UNSUPPORTED
+    a = list(ok); a[3] = None
+    assert lib.svg_quantize_fp8(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[4] = q                      # k8 overlaps q
+    assert lib.svg_quantize_fp8(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(ok); a[5] = ctypes.c_void_p((6 << 24) + 4)
+    assert lib.svg_quantize_fp8(*a) == L.SVG_ERR_INVALID_ARG
+    m128 = L.SvgMask(1, 8, 8, FAKE.value, FAKE.value, FAKE.value)
+    plan = lib.svg_attn_workspace_bytes(s128, 1)
+    att = [q8, k8, vt8, sc, q, s128, 0.125, ctypes.byref(m128), None, None, None,
+           ctypes.c_void_p(9 << 24), plan, None]
+    a = list(att); a[12] = plan - 1
+    assert lib.svg_block_sparse_attn_fp8(*a) == L.SVG_ERR_CAPACITY
+    a = list(att); a[5] = _shape()
+    assert lib.svg_block_sparse_attn_fp8(*a) == L.SVG_ERR_UNSUPPORTED
+    a = list(att); a[4] = q8                    # o overlaps q8
+    assert lib.svg_block_sparse_attn_fp8(*a) == L.SVG_ERR_INVALID_ARG
+    a = list(att); a[6] = 0.0
+    assert lib.svg_block_sparse_attn_fp8(*a) == L.SVG_ERR_INVALID_ARG
