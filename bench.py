@@ -218,6 +218,45 @@ def norm_rope_leg(w, s, classes, dev, stream, reps=50):
                     f"rope runs {rope[:3]}, theta 1e4, temporal heads token-major; not part of the layer step"}
 
 
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+
+
+def fp8_leg(w, s, q, k, v, layer, flop, o_bf16, stream, reps=20):
+    """The FP8 (E4M3) variant on the same layer input and head choice:
+    svg_quantize_fp8 and svg_block_sparse_attn_fp8 each timed over `reps`
+    calls after three warm-up calls; roofline against the FP8 dense peak;
+    relative L2 distance of its output from the bf16 path's."""
+    import torch
+    import block_sparse_attention_svg_amd as svg
+    ops8 = svg.svg_quantize_fp8(q, k, v, s, head_layout=layer.choice)
+    ws = torch.empty(max(svg.svg_attn_workspace_bytes(s, True), 1), dtype=torch.uint8, device=q.device)
+    o8 = torch.empty_like(q)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_q = timed(lambda: svg.svg_quantize_fp8(q, k, v, s, head_layout=layer.choice, out=ops8))
+    t_a = timed(lambda: svg.svg_block_sparse_attn_fp8(ops8, s, layer.scale, layer.cand, head_mask=layer.choice,
+                                                       head_layout=layer.choice, out=o8, workspace=ws))
+    d = (o8.float() - o_bf16.float())
+    rl = float(d.norm() / o_bf16.float().norm())
+    tf = flop / (t_a * 1e-3) / 1e12
+    return {"attention_ms": round(t_a, 4), "attention_tflops": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+            "quantize_ms": round(t_q, 4), "rel_l2_vs_bf16": round(rl, 4),
+            "note": "E4M3 q, k, v (one scale per tensor and head), E4M3 weights for PV, fp32 softmax; "
+                    "same head choice and masks as the bf16 step; not part of the bf16 layer step"}
+
+
 def permute_leg(w, s, x, head_sel, n_temporal, stream, reps=50):
     """svg_permute (frame-major -> token-major) of one tensor's temporal heads,
     timed alone over `reps` calls after five warm-up calls (not part of the
@@ -389,6 +428,8 @@ def main():
         out["layout_hbm_frac"] = round(out["layout_gbs"] / PEAK_HBM_GBS, 4)
         out["layout_bytes"] = moved
         out["permute"] = permute_leg(w, s, k, layer.choice, n_temporal, stream)
+        if w.block == 128:
+            out["fp8"] = fp8_leg(w, s, q, k, v, layer, flop, o, stream)
         kv_bytes = 2 * w.B * w.H * tensor_bytes
         out["profile_gbs"] = round(kv_bytes / (per["profile"] * 1e-3) / 1e9, 1)
         out["profile_share"] = round(per["profile"] / ms_step, 4)

@@ -366,6 +366,18 @@ struct Cfg2 {
   __host__ __device__ static constexpr int at(int row, int chunk) {
     return (row % NI) * SEGB + (row / NI) * W + chunk * 16;
   }
+  // FP8 tiles of 128-byte rows (D = 128): the 8 rows s + 16 j of segment s
+  // sit in 128-byte slots slot(j) (bits 0 and 1 of j exchanged), so that the
+  // 32 rows one half-wave reads together (32 t + n, n < 32) fall on 32
+  // distinct 16-byte bank positions modulo 512 bytes (slots 0 and 2 of the
+  // segments 1040 bytes apart); the 16-row stagger of the plain layout gives
+  // 2-way conflicts there.
+  static constexpr bool SLOTS = F8 && KNI == 16 && VNI == 16 && KW == 128 && VW == 128;
+  __host__ __device__ static constexpr int slot(int j) { return (j & 4) | ((j & 1) << 1) | ((j & 2) >> 1); }
+  // byte offset of rows 32 t + n relative to rows n (any n < 32)
+  __host__ __device__ static constexpr int tile_off(int t, int plain) {
+    return SLOTS ? (4 * (t >> 1) + (t & 1)) * 128 : t * plain;
+  }
 };
 
 // The merged key-block sequence of a workgroup's two mask rows (the skip list
@@ -592,7 +604,7 @@ __device__ __forceinline__ void mfma_qk8(const char* kb_lds, int k_lane, const i
     if (kt + 1 < C::KT) {
 #pragma unroll
       for (int kk = 0; kk < C::DK8; ++kk)
-        nxt[kk] = lds_32bytes(kb_lds + k_lane + (kt + 1) * KT_OFF + kk * 64);
+        nxt[kk] = lds_32bytes(kb_lds + k_lane + C::tile_off(kt + 1, KT_OFF) + kk * 64);
     }
     __builtin_amdgcn_sched_barrier(0);
     sacc[kt] = f32x16{};
@@ -612,13 +624,13 @@ __device__ __forceinline__ void mfma_pv8(const char* vb_lds, int v_lane, const i
   constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
   i32x8 cur[C::DT], nxt[C::DT];
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) cur[dt] = lds_32bytes(vb_lds + v_lane + dt * DT_OFF);
+  for (int dt = 0; dt < C::DT; ++dt) cur[dt] = lds_32bytes(vb_lds + v_lane + C::tile_off(dt, DT_OFF));
 #pragma unroll
   for (int g = 0; g < C::PG; ++g) {
     if (g + 1 < C::PG) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
-        nxt[dt] = lds_32bytes(vb_lds + v_lane + dt * DT_OFF + (g + 1) * 64);
+        nxt[dt] = lds_32bytes(vb_lds + v_lane + C::tile_off(dt, DT_OFF) + (g + 1) * 64);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -987,8 +999,12 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
 
   // Copies of a group: wave w4 takes the tile's segments w4*PW .. w4*PW+PW-1.
   // Per lane, the global source offset is lane_src + s * W for segment s.
-  const uint32_t k_lane_src = (lane / (C::KW / 16)) * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
-  const uint32_t v_lane_src = (lane / (C::VW / 16)) * C::VNI * C::VW + (lane % (C::VW / 16)) * 16;
+  // (128-byte rows: the lane filling slot l / 8 of a segment fetches that
+  // slot's row, s + 16 slot(l / 8))
+  const int row_of_lane = C::SLOTS ? C::slot(lane / 8) : lane / (C::KW / 16);
+  const uint32_t k_lane_src = row_of_lane * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
+  const uint32_t v_lane_src = (C::SLOTS ? row_of_lane : lane / (C::VW / 16)) * C::VNI * C::VW +
+                              (lane % (C::VW / 16)) * 16;
   const uint32_t k_w4_src = w4 * C::KPW * C::KW, v_w4_src = w4 * C::VPW * C::VW;
   // K rows past N (ragged last block) fall outside the block's buffer range
   // and are never fetched: their scores are masked to -inf.  A block that
@@ -1051,8 +1067,10 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
   // bf16: K row srow (+32 kt), chunk h (+2 kk); V^T row n (+32 dt), chunk h
   // (+2 s).  FP8: K row n, chunk 2h (+4 kk); V^T row n, chunk 2h (+4 g).
   const int srow = F8 ? n : swap_bits23(n);
-  const int k_lane = C::template at<C::KNI, C::KW>(srow, F8 ? 2 * h : h);
-  const int v_lane = C::template at<C::VNI, C::VW>(n, F8 ? 2 * h : h);
+  const int k_lane = C::SLOTS ? (srow % 16) * C::SEGB + C::slot(srow / 16) * 128 + 32 * h
+                              : C::template at<C::KNI, C::KW>(srow, F8 ? 2 * h : h);
+  const int v_lane = C::SLOTS ? (n % 16) * C::SEGB + C::slot(n / 16) * 128 + 32 * h
+                              : C::template at<C::VNI, C::VW>(n, F8 ? 2 * h : h);
   float c2 = a.scale_log2;
   float o_scale = 1.f;   // FP8: V's dequantization factor
   if constexpr (F8) {

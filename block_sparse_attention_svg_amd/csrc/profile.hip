@@ -102,8 +102,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void profile_partial_kernel(ProfileArgs a, Geo g) {
   using C = PCfg<D>;
   __shared__ uint4 lds[C::STAGES * C::STRIDE + 64];   // ring stages, then a 1-KB sink
-  __shared__ uint32_t rowS[kQ][kMaxWords];
-  __shared__ uint32_t rowT[kQ][kMaxWords];
+  // rows padded to an odd word count: the 16 samples of a wave look up the
+  // same word index at once, which then falls in 16 different banks
+  __shared__ uint32_t rowS[kQ][kMaxWords + 1];
+  __shared__ uint32_t rowT[kQ][kMaxWords + 1];
   __shared__ int blkT[C::STAGES][kTK];
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
