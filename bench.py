@@ -45,6 +45,8 @@ def parse():
                     choices=["tiny", "cogvideox", "wan720p", "hunyuan720p", "static_wan720p"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample (0 disables it)")
+    ap.add_argument("--sustained-seconds", type=float, default=2.0,
+                    help="seconds of the dense-MFMA probe per data type (0 disables it)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain device copy of 1 GiB (HBM counter calibration)")
     return ap.parse_args()
@@ -221,6 +223,42 @@ def norm_rope_leg(w, s, classes, dev, stream, reps=50):
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 
 
+def phase(name, what):
+    """Wall-clock stamp of a phase on stderr (lines up external power / clock
+    samples with the work)."""
+    print(f"[phase] {name} {what} {time.time():.3f}", file=sys.stderr, flush=True)
+
+
+def sustained_mfma_leg(stream, seconds):
+    """Dense MFMA rate the board sustains right after the timed steps, from
+    svg_mfma_peak_probe (products on register operands only, one workgroup of
+    8 waves per CU): bf16, then FP8, each launched back to back for `seconds`
+    after one warm-up launch; rate = FLOP / event time."""
+    import torch
+    import block_sparse_attention_svg_amd as svg
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(n_cu * 512, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fp8, rounds in (("bf16", False, 2000), ("fp8", True, 1000)):   # about 1 ms per launch
+        svg.svg_mfma_peak_probe(fp8, rounds, sink)
+        torch.cuda.synchronize()
+        phase(f"mfma probe {name}", "start")
+        t0, flop, ms = time.time(), 0.0, 0.0
+        while time.time() - t0 < seconds:
+            e0.record(stream)
+            for _ in range(20):
+                flop += svg.svg_mfma_peak_probe(fp8, rounds, sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1)
+        phase(f"mfma probe {name}", "end")
+        res[f"{name}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    res["note"] = ("back-to-back 32x32 MFMAs on register operands, no memory or LDS traffic: the rate the "
+                   "board's power limit allows for dense matrix work right now, on this GPU")
+    return res
+
+
 def fp8_leg(w, s, q, k, v, layer, flop, o_bf16, stream, reps=20):
     """The FP8 (E4M3) variant on the same layer input and head choice:
     svg_quantize_fp8 and svg_block_sparse_attn_fp8 each timed over `reps`
@@ -356,11 +394,13 @@ def main():
     evs = [mk() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    phase("timed steps", "start")
     t_start.record(stream)
     for t in range(args.steps):
         step(args.warmup + t, evs[t])
     t_end.record(stream)
     torch.cuda.synchronize()
+    phase("timed steps", "end")
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
@@ -429,7 +469,9 @@ def main():
         out["layout_bytes"] = moved
         out["permute"] = permute_leg(w, s, k, layer.choice, n_temporal, stream)
         if w.block == 128:
+            phase("fp8 leg", "start")
             out["fp8"] = fp8_leg(w, s, q, k, v, layer, flop, o, stream)
+            phase("fp8 leg", "end")
         kv_bytes = 2 * w.B * w.H * tensor_bytes
         out["profile_gbs"] = round(kv_bytes / (per["profile"] * 1e-3) / 1e9, 1)
         out["profile_share"] = round(per["profile"] / ms_step, 4)
@@ -463,6 +505,12 @@ def main():
                                    "note": "row attention patterns of all heads + per-frame cosines; "
                                            "FLOP = one QK^T (computed twice)"}
         del r_ws
+    if args.sustained_seconds > 0:
+        sus = sustained_mfma_leg(stream, args.sustained_seconds)
+        sus["attention_frac_of_bf16"] = round(achieved / sus["bf16_tflops"], 4)
+        if "fp8" in out:
+            sus["fp8_attention_frac_of_fp8"] = round(out["fp8"]["attention_tflops"] / sus["fp8_tflops"], 4)
+        out["mfma_sustained"] = sus
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, classes, args.cpu_seconds)
     else:

@@ -14,6 +14,7 @@ from .ops import (
     svg_row_similarity_workspace_bytes, svg_qk_norm_rope, svg_vt_bytes, svg_prepare_kv,
     svg_noalloc_scratch_bytes, svg_block_sparse_attn_noalloc,
     Fp8Operands, svg_fp8_vt_bytes, svg_quantize_fp8, svg_block_sparse_attn_fp8,
+    svg_mfma_peak_probe,
 )
 from .layer import OnlineSparseAttention, StaticSparseAttention, attention_flops, kept_pairs_per_mask
 from ._lib import SvgError, LIB_PATH
@@ -27,6 +28,7 @@ __all__ = [
     "svg_row_similarity_workspace_bytes", "svg_qk_norm_rope", "svg_vt_bytes", "svg_prepare_kv",
     "svg_noalloc_scratch_bytes", "svg_block_sparse_attn_noalloc",
     "Fp8Operands", "svg_fp8_vt_bytes", "svg_quantize_fp8", "svg_block_sparse_attn_fp8",
+    "svg_mfma_peak_probe",
     "OnlineSparseAttention", "StaticSparseAttention", "attention_flops", "kept_pairs_per_mask",
     "SvgError", "LIB_PATH",
 ]

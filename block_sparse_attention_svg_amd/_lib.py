@@ -68,6 +68,7 @@ _SIGS = {
     "svg_eps_schedule": (_I, [_I, _I, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
     "svg_row_similarity_workspace_bytes": (ctypes.c_size_t, [SvgShape]),
     "svg_row_similarity": (_I, [_P, _P, SvgShape, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "svg_mfma_peak_probe": (_I, [_I, _I, _P, ctypes.c_int64, ctypes.POINTER(ctypes.c_double), _P]),
     "svg_status_string": (ctypes.c_char_p, [_I]),
     "svg_last_error": (ctypes.c_char_p, []),
     "svg_version": (ctypes.c_char_p, []),

@@ -441,3 +441,14 @@ def svg_eps_schedule(t: int, T: int, eps_first: float = 0.99, eps_last: float = 
 
 def svg_version() -> str:
     return L.lib().svg_version().decode()
+
+
+def svg_mfma_peak_probe(fp8: bool, rounds: int, sink: torch.Tensor) -> float:
+    """Enqueue one launch of the dense-MFMA probe (a measurement aid, not part
+    of the attention path); returns the launch's FLOP.  sink: float32 device
+    tensor of at least n_CU * 512 elements."""
+    _need(sink, "sink", torch.float32)
+    flop = ctypes.c_double(0.0)
+    L.check("svg_mfma_peak_probe", L.lib().svg_mfma_peak_probe(int(bool(fp8)), int(rounds), _ptr(sink),
+                                                               sink.numel(), ctypes.byref(flop), _stream()))
+    return float(flop.value)

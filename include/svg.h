@@ -389,6 +389,22 @@ svg_status svg_restrict_anchor_rows(uint8_t* masks, int n_masks, svg_shape s,
 svg_status svg_calibrate_masks(const double* energy, int n_masks, int n_qb, int n_kb,
                                double eps, uint8_t* out, void* stream);
 
+/* ---- measurement aid (not part of the attention path) ---------------------- */
+/* Dense matrix-core rate this GPU sustains under its power limit: one
+ * workgroup of 8 wavefronts per CU, each issuing `rounds` x 16 back-to-back
+ * 32x32 MFMAs (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x64_f8f6f4 when
+ * fp8 = 1) on operands held in registers: no memory or LDS traffic.  The
+ * rate (FLOP / kernel time) bounds what any kernel with the same products
+ * reaches on this board at this moment; the attention's rate is reported
+ * beside it.  sink: device float [sink_floats] written with junk (one float
+ * per thread, >= n_CU * 512 floats); flop (host out): FLOP of the launch,
+ * n_CU * 8 * rounds * 16 * 2 * 32 * 32 * K (K = 16 bf16, 64 FP8).
+ * Errors: SVG_ERR_INVALID_ARG for fp8 outside {0, 1}, rounds outside
+ * [1, 2^20] or NULL pointers; SVG_ERR_HIP without a device;
+ * SVG_ERR_CAPACITY for a short sink. */
+svg_status svg_mfma_peak_probe(int fp8, int rounds, float* sink, int64_t sink_floats, double* flop,
+                               void* stream);
+
 /* ---- errors -------------------------------------------------------------- */
 const char* svg_status_string(svg_status st);
 const char* svg_last_error(void);

@@ -317,3 +317,14 @@ def test_fp8_validation():
     assert lib.svg_block_sparse_attn_fp8(*a) == L.SVG_ERR_INVALID_ARG
     a = list(att); a[6] = 0.0
     assert lib.svg_block_sparse_attn_fp8(*a) == L.SVG_ERR_INVALID_ARG
+
+
+def test_mfma_peak_probe_validation():
+    """The measurement probe checks its arguments before any HIP call."""
+    lib = L.lib()
+    flop = ctypes.c_double(0.0)
+    assert lib.svg_mfma_peak_probe(2, 10, FAKE, 1 << 20, ctypes.byref(flop), None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_mfma_peak_probe(0, 0, FAKE, 1 << 20, ctypes.byref(flop), None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_mfma_peak_probe(1, (1 << 20) + 1, FAKE, 1 << 20, ctypes.byref(flop), None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_mfma_peak_probe(0, 10, None, 1 << 20, ctypes.byref(flop), None) == L.SVG_ERR_INVALID_ARG
+    assert lib.svg_mfma_peak_probe(0, 10, FAKE, 1 << 20, None, None) == L.SVG_ERR_INVALID_ARG
