@@ -289,56 +289,6 @@ __global__ __launch_bounds__(BLK / 32 * 64) void attn_fwd_kernel(AttnArgs a) {
 // token-major Q / V / O twin is not given reads Q and V from the frame-major
 // tensors and writes O to them through the layout permutation.
 // ---------------------------------------------------------------------------
-#define LDS_AS __attribute__((address_space(3)))
-
-// A byte range of global memory as a buffer resource, for 16-byte
-// global->LDS copies (buffer_load_dwordx4 ... lds): lane offsets are 32-bit
-// VGPRs, a wave-uniform offset goes in an SGPR, the range check drops reads
-// past the end (nothing is fetched for them), and the LDS destination of the
-// wavefront instruction is the M0 base (lane l writes 16 bytes at base + 16 l).
-struct LdsCopySrc {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r;
-#endif
-  __device__ __forceinline__ LdsCopySrc(const void* base, int bytes) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-#endif
-  }
-  __device__ __forceinline__ void copy16(uint32_t lane_off, uint32_t uniform_off, uint32_t lds_addr) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(uintptr_t)lds_addr, 16, lane_off,
-                                             uniform_off, 0, 0);
-#endif
-  }
-};
-
-// Scalar add of a compile-time constant, kept at its point of use: the
-// per-copy offsets are loop-invariant, and hoisted out of the loop all
-// together they would exceed the scalar registers and be spilled.
-template <int C>
-__device__ __forceinline__ uint32_t sadd(uint32_t a) {
-  uint32_t r;
-  asm volatile("s_add_u32 %0, %1, %2" : "=s"(r) : "s"(a), "i"(C) : "scc");
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(uintptr_t)(LDS_AS const void*)p;
-}
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for_from(F& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for_from<I + 1, N>(f);
-  }
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_from<0, N>(f);
-}
 
 template <int D, bool F8 = false>
 struct Cfg2 {

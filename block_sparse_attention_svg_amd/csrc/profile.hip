@@ -46,8 +46,6 @@ constexpr int kMaxWords = 32;   // bitmap words per row held in LDS (nB <= 1024)
 constexpr int kChunkKeys = 32768;
 constexpr float kRescaleLog2 = 24.0f;   // weights stay below 2^24 between moves
 
-#define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
 
 template <int D>
 struct PCfg {
@@ -56,8 +54,12 @@ struct PCfg {
   static constexpr int CPR = D / 8;      // 16-byte chunks per K / V row
   static constexpr int KROW = CPR + 1;   // padded K row (D+8 elements): conflict-free b128 fetches
   static constexpr int VROW = CPR + 4;   // padded V row (D+32): conflict-free transposing fetches
-  static constexpr int KCH = kTK * KROW, VCH = kTK * VROW, BUF = KCH + VCH;
-  static constexpr int SEGS = (BUF + 63) / 64;
+  static constexpr int KCH = kTK * KROW, VCH = kTK * VROW;
+  // K rows and V rows take whole 1-KB segments of their own, so that one
+  // copy instruction reads from one tensor only
+  static constexpr int KSEG = (KCH + 63) / 64, VSEG = (VCH + 63) / 64;
+  static constexpr int SEGS = KSEG + VSEG;
+  static constexpr int KOFF = KSEG * 64;       // first chunk of the V rows in a stage
   static constexpr int SPW = (SEGS + 3) / 4;   // load instructions per wave per tile
   static constexpr int STAGES = 3;             // ring of tiles: two loads in flight
   static constexpr int STRIDE = SEGS * 64;     // chunks per stage (whole 1-KB segments)
@@ -149,46 +151,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int k_end = min(N, k_begin + a.chunk_keys);
   const int n_tiles = (k_end - k_begin + kTK - 1) / kTK;
 
-  // this thread's 16-byte global->LDS copies of one tile (K chunks, then V
-  // chunks; lanes on row padding idle): byte offset inside the tile's rows,
-  // bit 30 marking V, -1 when idle
-  int src[C::SPW];
+  // This thread's 16-byte global->LDS copies of one tile: copy u of wave w
+  // fills segment 4u + w of the stage (K segments first, then V; segments
+  // past the stage go to a 1-KB sink).  off[u] = byte offset of the lane's
+  // chunk within the tile's rows (row r, chunk c: (r * D + 8 c) * 2), or
+  // kNoFetch for lanes on row padding.  Every wave issues exactly SPW copies
+  // per tile, so vmcnt(SPW) waits for precisely the oldest tile in flight.
+  constexpr uint32_t kNoFetch = 0x80000000u;   // beyond any tile's buffer range: nothing is read
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t off[C::SPW];
 #pragma unroll
   for (int u = 0; u < C::SPW; ++u) {
-    const int p = (u * 4 + wave) * 64 + lane;
-    int off = -1;
-    if (p < C::KCH) {
-      const int r = p / C::KROW, c = p % C::KROW;
-      if (c < C::CPR) off = (r * D + c * 8) * 2;
-    } else if (p < C::BUF) {
-      const int r = (p - C::KCH) / C::VROW, c = (p - C::KCH) % C::VROW;
-      if (c < C::CPR) off = ((r * D + c * 8) * 2) | (1 << 30);
+    const int seg = u * 4 + wave;
+    uint32_t o = kNoFetch;
+    if (seg < C::KSEG) {
+      const int p = seg * 64 + lane, r = p / C::KROW, c = p % C::KROW;
+      if (p < C::KCH && c < C::CPR) o = uint32_t(r * D + c * 8) * 2;
+    } else if (seg < C::SEGS) {
+      const int p = (seg - C::KSEG) * 64 + lane, r = p / C::VROW, c = p % C::VROW;
+      if (p < C::VCH && c < C::CPR) o = uint32_t(r * D + c * 8) * 2;
     }
-    src[u] = off;
+    off[u] = o;
   }
-  // Every wave issues exactly SPW copies per tile, so vmcnt(SPW) waits for
-  // precisely the oldest tile in flight.  The LDS destination of a copy is
-  // wave-uniform: lanes on row padding fill padding of their own stage, and
-  // segments past the tile go to a sink.
-  char* lds_b = reinterpret_cast<char*>(lds);
+  const uint32_t lds_base = lds_addr_of(lds);
   auto stage = [&](int key0, int b) {
-    char* sbase = lds_b + b * C::STRIDE * 16;
-    const int last = k_end - 1 - key0;   // rows past the chunk read its last row (masked later)
+    // buffer resources over the tile's rows that exist (rows past N are not
+    // fetched; in a tile that ends past N the lanes of those rows read the
+    // last row instead, so the stage holds finite values throughout)
+    const int rows = min(kTK, k_end - key0);
+    const LdsCopySrc ksrc(Kh + int64_t(key0) * D * 2, rows * D * 2);
+    const LdsCopySrc vsrc(Vh + int64_t(key0) * D * 2, rows * D * 2);
+    const uint32_t sbase = lds_base + b * C::STRIDE * 16;
+    auto issue = [&](auto ragged_c) {
+      constexpr bool RAGGED = decltype(ragged_c)::value;
 #pragma unroll
-    for (int u = 0; u < C::SPW; ++u) {
-      const int seg = u * 4 + wave;
-      int off = 0;
-      const char* base = Kh;
-      if (src[u] >= 0) {
-        off = src[u] & ~(1 << 30);
-        base = (src[u] & (1 << 30)) ? Vh : Kh;
-        const int r = off / (D * 2);
-        if (r > last) off += (last - r) * D * 2;
+      for (int u = 0; u < C::SPW; ++u) {
+        const int seg = u * 4 + wave_u;   // wave-uniform: scalar selects, no branches
+        uint32_t o = off[u];
+        if constexpr (RAGGED) {
+          const int r = int(o) / (D * 2);
+          if (o != kNoFetch && r >= rows) o -= uint32_t(r - rows + 1) * D * 2;
+        }
+        const LdsCopySrc& src = seg < C::KSEG ? ksrc : vsrc;
+        src.copy16(o, 0, seg < C::SEGS ? sbase + seg * 1024 : lds_base + C::DUMMY * 16);
       }
-      char* dst = seg < C::SEGS ? sbase + seg * 64 * 16 : lds_b + C::DUMMY * 16;
-      __builtin_amdgcn_global_load_lds((GLB_AS void*)(base + int64_t(key0) * D * 2 + off),
-                                       (LDS_AS void*)dst, 16, 0, 0);
-    }
+    };
+    if (rows < kTK) issue(std::true_type{});   // the chunk's last tile, past N
+    else issue(std::false_type{});
     if (tid < kTK) {
       const int key = min(key0 + tid, k_end - 1);
       blkT[b][tid] = token_major(key, g) >> g.blk_log2;
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
 
   const int k_lane = ((8 * (n >> 2) + (n & 3)) * C::KROW + grp) * 16;   // tile 0, kk 0
-  const int v_lane = C::KCH * 16 + ((8 * grp + (n >> 2)) * C::VROW) * 16 + ((n & 3) * 4) * 2;
+  const int v_lane = C::KOFF * 16 + ((8 * grp + (n >> 2)) * C::VROW) * 16 + ((n & 3) * 4) * 2;
   const float c2 = a.scale_log2;
 
   // Admission of this lane's 8 keys of a tile (8 * grp + i) for its sample:
@@ -253,7 +262,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     barrier_lds();     // everyone's copies landed; stage (t+2)%3 is no longer read
     if (t + 2 < n_tiles) stage(key0 + 2 * kTK, (t + 2) % C::STAGES);
     if (t + 1 < n_tiles) adm_next = admission(key0 + kTK, (t + 1) % C::STAGES);
-    const char* lb = lds_b + b * C::STRIDE * 16;
+    // 32-bit LDS address of the stage: constant parts of the operand
+    // addresses then fold into the instructions' offset fields
+    const uint32_t lb = lds_base + b * C::STRIDE * 16;
 #pragma unroll
     for (int half = 0; half < kTK / 32; ++half) {
       // ---- S^T for 32 keys: two 16x16 tiles; lane (n, grp) gets keys 8*grp + i
@@ -263,9 +274,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         s2[tile] = f32x4{};
 #pragma unroll
         for (int kk = 0; kk < C::DK; ++kk) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(
+          const bf16x8 kop = *(const LDS_AS bf16x8*)(uintptr_t)(
               lb + k_lane + ((half * 32 + 4 * tile) * C::KROW + 4 * kk) * 16);
-          s2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(raw), qreg[kk], s2[tile], 0, 0, 0);
+          s2[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], s2[tile], 0, 0, 0);
         }
       }
       const bool inS = (adm >> 8) & 1u;
@@ -282,17 +293,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           s_live = inS;
         }
       }
+      // class bits of the lane's 8 keys: T-kept / T-skipped among the keys
+      // that exist (keys past the chunk belong to neither class; lanes of
+      // samples past n_samples compute on zero rows, and their records are
+      // never read)
+      uint32_t vbits = 0xffu;
+      if (key0 + kTK > k_end) {
+        const int nv = k_end - (key0 + half * 32 + 8 * grp);
+        vbits = nv >= 8 ? 0xffu : nv <= 0 ? 0u : (1u << nv) - 1u;
+      }
+      const uint32_t in_bits = adm & vbits, out_bits = ~adm & vbits;
       float x[8];
-      bool inT[8];
+      bool inT[8], outT[8];
       float m_in = -INFINITY, m_out = -INFINITY;   // this lane's max over T-kept / T-skipped keys
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int kl = half * 32 + 8 * grp + i;
-        inT[i] = (adm >> i) & 1u;
-        const bool ok = svalid && key0 + kl < k_end;
-        x[i] = ok ? s2[i >> 2][i & 3] : -INFINITY;
+        inT[i] = (in_bits >> i) & 1u;
+        outT[i] = (out_bits >> i) & 1u;
+        x[i] = s2[i >> 2][i & 3];
         m_in = fmaxf(m_in, inT[i] ? x[i] : -INFINITY);
-        m_out = fmaxf(m_out, inT[i] ? -INFINITY : x[i]);
+        m_out = fmaxf(m_out, outT[i] ? x[i] : -INFINITY);
       }
       m_in *= c2;
       m_out *= c2;
@@ -325,14 +345,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const float p = fast_exp2(__builtin_fmaf(x[i], c2, -(inT[i] ? mL[0] : mL[1])));
         const __bf16 pb = (__bf16)p;
         pin[i] = inT[i] ? pb : (__bf16)0.0f;
-        pout[i] = inT[i] ? (__bf16)0.0f : pb;
+        pout[i] = outT[i] ? pb : (__bf16)0.0f;
       }
       // ---- U^T += V^T P^T for the two live classes; Z from an all-ones operand
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const char* p0 = lb + v_lane + (half * 32 * C::VROW) * 16 + dt * 32;
-        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p0);
-        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p0 + 4 * C::VROW * 16));
+        const uint32_t p0 = lb + v_lane + (half * 32 * C::VROW) * 16 + dt * 32;
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(uintptr_t)p0);
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(uintptr_t)(p0 + 4 * C::VROW * 16));
         const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         uL[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pin, uL[0][dt], 0, 0, 0);
         uL[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pout, uL[1][dt], 0, 0, 0);
