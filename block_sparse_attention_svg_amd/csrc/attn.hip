@@ -323,10 +323,16 @@ struct Cfg2 {
   // segments 1040 bytes apart); the 16-row stagger of the plain layout gives
   // 2-way conflicts there.
   static constexpr bool SLOTS = F8 && KNI == 16 && VNI == 16 && KW == 128 && VW == 128;
+  // The bf16 K tile at D = 64 has the same geometry (16 segments of 128-byte
+  // rows) and takes the same slots; its V^T rows are 256 bytes and need none.
+  static constexpr bool KSLOTS = KNI == 16 && KW == 128;
   __host__ __device__ static constexpr int slot(int j) { return (j & 4) | ((j & 1) << 1) | ((j & 2) >> 1); }
   // byte offset of rows 32 t + n relative to rows n (any n < 32)
   __host__ __device__ static constexpr int tile_off(int t, int plain) {
     return SLOTS ? (4 * (t >> 1) + (t & 1)) * 128 : t * plain;
+  }
+  __host__ __device__ static constexpr int tile_off_k(int t, int plain) {
+    return KSLOTS ? (4 * (t >> 1) + (t & 1)) * 128 : t * plain;
   }
 };
 
@@ -409,14 +415,14 @@ __device__ __forceinline__ void mfma_qk(const char* kb_lds, int k_lane, const bf
 #pragma unroll
   for (int kt = 0; kt < C::KT; ++kt) {
     sacc[kt] = f32x16{};
-    cur[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + kt * 256);   // rows +32
+    cur[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + C::tile_off_k(kt, 256));   // rows +32 kt
   }
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
     if (kk + 1 < C::DK) {
 #pragma unroll
       for (int kt = 0; kt < C::KT; ++kt)
-        nxt[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + kt * 256 + (kk + 1) * 32);
+        nxt[kt] = *reinterpret_cast<const uint4*>(kb_lds + k_lane + C::tile_off_k(kt, 256) + (kk + 1) * 32);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -696,7 +702,10 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
 
   // Copies of a group: wave w4 takes the tile's segments w4*PW .. w4*PW+PW-1.
   // Per lane, the global source offset is lane_src + s * W for segment s.
-  const uint32_t k_lane_src = (lane / (C::KW / 16)) * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
+  // (128-byte K rows: the lane filling slot l / 8 of a segment fetches that
+  // slot's row, s + 16 slot(l / 8))
+  const int k_row_of_lane = C::KSLOTS ? C::slot(lane / 8) : lane / (C::KW / 16);
+  const uint32_t k_lane_src = k_row_of_lane * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
   const uint32_t v_lane_src = (lane / (C::VW / 16)) * C::VNI * C::VW + (lane % (C::VW / 16)) * 16;
   const uint32_t k_w4_src = w4 * C::KPW * C::KW, v_w4_src = w4 * C::VPW * C::VW;
   // K rows past N (ragged last block) fall outside the block's buffer range
@@ -757,7 +766,8 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
 
   const int srow = swap_bits23(n);
   const float c2 = a.scale_log2;
-  const int k_lane = C::template at<C::KNI, C::KW>(srow, h);   // K row srow (+32 kt), chunk h (+2 kk)
+  const int k_lane = C::KSLOTS ? (srow % 16) * C::SEGB + C::slot(srow / 16) * 128 + 16 * h
+                               : C::template at<C::KNI, C::KW>(srow, h);   // K row srow (+32 kt), chunk h (+2 kk)
   const int v_lane = C::template at<C::VNI, C::VW>(n, h);      // V^T row n (+32 dt), chunk h (+2 s)
 
   // cur: block j (K_j staged / being used); prev: block j-1 (V_{j-1})
