@@ -1398,6 +1398,11 @@ __global__ __launch_bounds__(256) void vt_prep_kernel(const __bf16* __restrict__
                                                       __bf16* __restrict__ kp, int N, int nKB,
                                                       AttnArgs a) {
   constexpr int BLK = 128, CPR = D / 8, TASKS = (BLK / 8) * CPR;
+  constexpr int KC = BLK / 8;          // 16-byte chunks per V^T row (8 keys each)
+  // V^T block staged in LDS: row d holds 16 chunks of 8 keys; chunk c of row
+  // d sits at position c ^ ((d / 8) % 16), so that the 16 lanes writing the
+  // rows 8 dc + j of one chunk column hit 16 different bank groups
+  __shared__ uint4 tile[D * KC];
   const int kb = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
   const bool tm = head_layout && head_layout[bh] != 0;
@@ -1413,21 +1418,33 @@ __global__ __launch_bounds__(256) void vt_prep_kernel(const __bf16* __restrict__
       if (r < N) kdst[int64_t(r) * CPR + c % CPR] = ksrc[int64_t(frame_major_of(r, a)) * CPR + c % CPR];
     }
   }
-  if (t >= TASKS) return;
-  const bool gather = tm && vp == nullptr;   // token-major keys read from v through the permutation
-  const uint4* src = reinterpret_cast<const uint4*>((tm && !gather ? vp : v) + int64_t(bh) * N * D);
-  const int dc = t % CPR, kg = t / CPR;
-  uint4 rows[8], cols[8];
+  if (t < TASKS) {
+    // thread (dc, kg): keys 8 kg .. 8 kg + 7, dims 8 dc .. 8 dc + 7; a
+    // wavefront reads whole 2D-byte rows
+    const bool gather = tm && vp == nullptr;   // token-major keys read from v through the permutation
+    const uint4* src = reinterpret_cast<const uint4*>((tm && !gather ? vp : v) + int64_t(bh) * N * D);
+    const int dc = t % CPR, kg = t / CPR;
+    uint4 rows[8], cols[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = kb * BLK + 8 * kg + i;
-    const int row = gather && key < N ? frame_major_of(key, a) : key;
-    rows[i] = key < N ? src[int64_t(row) * CPR + dc] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int key = kb * BLK + 8 * kg + i;
+      const int row = gather && key < N ? frame_major_of(key, a) : key;
+      rows[i] = key < N ? src[int64_t(row) * CPR + dc] : make_uint4(0, 0, 0, 0);
+    }
+    transpose8x8(rows, cols);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[(8 * dc + j) * KC + (kg ^ (dc % KC))] = cols[j];
   }
-  transpose8x8(rows, cols);
+  __syncthreads();
+  // the V^T block leaves as whole 256-byte rows: lane (c, r) stores chunk c
+  // of row r
   uint4* dst = reinterpret_cast<uint4*>(vt + (int64_t(bh) * nKB + kb) * BLK * D);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dst[(8 * dc + j) * (BLK / 8) + kg] = cols[j];
+  for (int u = 0; u < D * KC / 256; ++u) {
+    const int e = t + u * 256;
+    const int r = e / KC, c = e % KC;
+    dst[e] = tile[r * KC + (c ^ ((r / 8) % KC))];
+  }
 }
 
 template <int D, int BLK>
