@@ -323,12 +323,13 @@ def test_fused_layout_batch2_mixed_layouts():
     assert torch.equal(lse_t, lse_f)
 
 
-def test_prepare_kv_bit_exact():
+@pytest.mark.parametrize("D", [128, 64])
+def test_prepare_kv_bit_exact(D):
     """svg_prepare_kv: every head's V block-transposed in its layout (keys past
     N zero) and the layout-1 heads' K token-major, against the oracle's
     permutation; K rows of layout-0 heads are left untouched."""
-    banner("prepare kv")
-    B, H, F, Hs, Ws, text, D = 2, 3, 5, 6, 22, 41, 128
+    banner("prepare kv", D)
+    B, H, F, Hs, Ws, text = 2, 3, 5, 6, 22, 41
     N = F * Hs * Ws + text
     g = torch.Generator().manual_seed(95)
     k, v = (torch.randn(B, H, N, D, generator=g).to(torch.bfloat16) for _ in range(2))
