@@ -1389,7 +1389,8 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
 // through the permutation), and when kp is given the block's token-major K
 // rows are written there too ([SVG], layout transformation: the temporal
 // heads' keys made contiguous), so K and V cross HBM in one pass.  Each
-// thread transposes 8 keys x 8 dims in registers.
+// thread transposes 8 keys x 8 dims in registers; the block's V^T goes
+// through LDS and leaves as whole 256-byte rows.
 template <int D>
 __global__ __launch_bounds__(256) void vt_prep_kernel(const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ vp,
