@@ -33,7 +33,9 @@ METRIC = "effective TFLOP/s on kept blocks + ms/attention layer, Wan-720p shape,
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PMC_FILE = os.path.join(ROOT, "profiles", "attn_pmc_counters.json")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_svg_amd", "csrc", "attn.hip")
+# the attention kernel's sources: its file and the two headers it includes
+ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_svg_amd", "csrc", f)
+             for f in ("attn.hip", "attn_tiles.h", "mfma_common.h")]
 
 
 def parse():
@@ -57,16 +59,19 @@ def describe(w):
             f"{' + %d text' % w.text if w.text else ''} = {w.N} tokens, bf16, block {w.block}")
 
 
-def code_hash(path):
-    """Hash of a C++/HIP source with its comments and whitespace removed: the
-    counters recorded for the attention kernel stay valid across comment
-    edits and are dropped as soon as its code changes."""
+def code_hash(paths):
+    """Hash of C++/HIP sources (in the given order) with their comments and
+    whitespace removed: the counters recorded for the attention kernel stay
+    valid across comment edits and are dropped as soon as its code changes."""
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    text = re.sub(r"\s+", "", text)
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", "", text)
+        h.update(os.path.basename(path).encode() + b"\0" + text.encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, q, k, v, classes, budget_s):
@@ -428,7 +433,7 @@ def main():
         try:
             pmc = json.load(open(PMC_FILE))
             key = w.name
-            if pmc.get("attn_code_sha") == code_hash(ATTN_SRC) and key in pmc.get("workloads", {}):
+            if pmc.get("attn_code_sha") == code_hash(ATTN_SRCS) and key in pmc.get("workloads", {}):
                 traffic = pmc["workloads"][key]["hbm_bytes_per_launch"]
         except Exception:
             traffic = None

@@ -12,7 +12,10 @@
 // units); the second recomputes the scores, weighs them by exp2(s - lse) and
 // sums each block pair: per lane, then over the wave, then over the waves in
 // order, so the result is identical on every call.  fp32 arithmetic, float64
-// output for the threshold rule.
+// output for the threshold rule.  With 128-token blocks, energy_pp_kernel runs
+// the same arithmetic on the attention kernel's two-group schedule (two query
+// blocks per workgroup, matrix-core and VALU phases overlapped).
+#include "attn_tiles.h"
 #include "mfma_common.h"
 #include "svg_internal.h"
 
@@ -160,6 +163,182 @@ __global__ __launch_bounds__(BLK * 2, 2) void energy_kernel(const __bf16* __rest
   }
   __syncthreads();
   if (tid == 0) finish(nB - 1);
+}
+
+// 128-token blocks: the attention kernel's two-phase schedule.  One
+// workgroup of 8 wavefronts takes two query blocks of a head (rows 2p and
+// 2p + 1 of E): group 0 (waves 0-3) computes S^T of key block j on the
+// matrix cores while group 1 works on block j-1's scores on the VALU, then
+// the roles swap; K tiles reach double-buffered LDS through 16-byte
+// global->LDS copies issued by group 0 before its VALU phase.  Sweep 1 keeps
+// each query's running max and sum, sweep 2 the block sums, with the same
+// arithmetic in the same order as energy_kernel (the results are the same
+// bits).
+template <int D>
+__device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const __bf16* __restrict__ k, int N,
+                                            int nB, float c2, double* __restrict__ E, int pair, int bh) {
+  using C = Cfg2<D>;
+  // separate arrays per buffer, addressed with compile-time indices (the
+  // compiler then sees that copies in flight target the other buffer)
+  __shared__ uint4 kbuf0[C::KBYTES / 16], kbuf1[C::KBYTES / 16];
+  __shared__ float part[2][2][4];   // [block parity][group][wave]
+  char* const kb_lds[2] = {reinterpret_cast<char*>(kbuf0), reinterpret_cast<char*>(kbuf1)};
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = wave >> 2;
+  const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);
+  const int n = lane & 31, h = lane >> 5;
+  const int qb = 2 * pair + grp;
+  const bool has_row = qb < nB;
+  const __bf16* qh = q + int64_t(bh) * N * D;
+  const char* Kh = reinterpret_cast<const char*>(k + int64_t(bh) * N * D);
+  const int qi = qb * 128 + w4 * 32 + n;
+  const bool q_ok = qi < N;
+  bf16x8 qreg[C::DK];
+#pragma unroll
+  for (int kk = 0; kk < C::DK; ++kk) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (q_ok) u = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * kk + 8 * h);
+    qreg[kk] = as_bf16x8(u);
+  }
+  // K rows in natural order: register r of tile kt holds key 32 kt + 8 (r/4)
+  // + 4 h + r%4 for query n (the energy_kernel layout)
+  const int k_lane = C::KSLOTS ? (n % 16) * C::SEGB + C::slot(n / 16) * 128 + 16 * h
+                               : C::template at<C::KNI, C::KW>(n, h);
+  const int k_row_of_lane = C::KSLOTS ? C::slot(lane / 8) : lane / (C::KW / 16);
+  const uint32_t k_lane_src = k_row_of_lane * C::KNI * C::KW + (lane % (C::KW / 16)) * 16;
+  const uint32_t k_w4_src = w4 * C::KPW * C::KW;
+  auto copy_k = [&](int kb, const char* dst) {   // group 0; rows past N are not fetched
+    const bool exists = kb < nB;
+    const LdsCopySrc src(Kh + int64_t(exists ? kb : 0) * 128 * D * 2,
+                         exists ? min(128, N - kb * 128) * D * 2 : 0);
+    const uint32_t lds_w = lds_addr_of(dst) + w4 * C::KPW * C::SEGB;
+    static_for<C::KPW>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      src.copy16(k_lane_src, sadd<u * C::KW>(k_w4_src), sadd<u * C::SEGB>(lds_w));
+    });
+  };
+  f32x16 sacc[C::KT];
+  auto key_of = [&](int kb, int kt, int i) { return kb * 128 + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3); };
+
+  float m = -INFINITY, l = 0.f, lse2 = 0.f;
+  // sweep 1: running max and sum; sweep 2: block sums of exp2(s - lse)
+  auto stats = [&](int kb) {
+    if (kb * 128 + 128 > N) {   // the ragged last block: keys past N drop out
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key_of(kb, kt, i) >= N) sacc[kt][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+    mx = max_cross_half(mx) * c2;
+    const float m_new = fmaxf(m, mx);
+    float add = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) add += fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -m_new));
+    l = l * fast_exp2(m - m_new) + add;
+    m = m_new;
+  };
+  auto bsum = [&](int kb) {
+    float sum = 0.f;
+    if (kb * 128 + 128 > N) {
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+          sum += key_of(kb, kt, i) < N ? p : 0.f;
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+    }
+    if (!q_ok) sum = 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) part[kb & 1][grp][w4] = sum;   // summed after the iteration's barrier
+  };
+  double* erow = E + (int64_t(bh) * nB + qb) * nB;
+  // iteration j: K of block j in buffer j % 2; group 1 handles block j-1's
+  // scores in phase 1, group 0 block j's in phase 2
+  auto iteration = [&](int j, auto kbuf_c, auto second_c) {
+    constexpr int kbuf = decltype(kbuf_c)::value;
+    constexpr bool SECOND = decltype(second_c)::value;
+    const bool cur = j < nB, prev = j > 0;
+    if (grp == 0) {
+      if (cur) mfma_qk<D>(kb_lds[kbuf], k_lane, qreg, sacc);
+    } else if (prev) {
+      if constexpr (SECOND) bsum(j - 1);
+      else stats(j - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) {
+      copy_k(j + 1, kb_lds[kbuf ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cur) {
+        if constexpr (SECOND) bsum(j);
+        else stats(j);
+      }
+    } else if (cur) {
+      mfma_qk<D>(kb_lds[kbuf], k_lane, qreg, sacc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SECOND) {
+      // group 0's block j and group 1's block j-1 are complete: four wave
+      // sums each, added in wave order
+      if ((tid & 255) == 0) {
+        const int kbd = grp == 0 ? j : j - 1;
+        if (kbd >= 0 && kbd < nB && has_row) {
+          float t = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) t += part[kbd & 1][grp][w];
+          erow[kbd] = double(t);
+        }
+      }
+    }
+  };
+  auto sweep = [&](auto second_c) {
+    if (grp == 0) copy_k(0, kb_lds[0]);
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+    barrier_lds();
+    for (int j = 0; j <= nB; j += 2) {
+      iteration(j, std::integral_constant<int, 0>{}, second_c);
+      if (j + 1 <= nB) iteration(j + 1, std::integral_constant<int, 1>{}, second_c);
+    }
+  };
+  sweep(std::false_type{});
+  lse2 = m + __log2f(l + __shfl_xor(l, 32, 64));
+  barrier_lds();   // every wave is done with the tiles of sweep 1
+  sweep(std::true_type{});
+}
+
+// 128-token blocks: the attention kernel's two-phase schedule.  One
+// workgroup of 8 wavefronts takes two query blocks of a head (rows 2p and
+// 2p + 1 of E): group 0 (waves 0-3) computes S^T of key block j on the
+// matrix cores while group 1 works on block j-1's scores on the VALU, then
+// the roles swap; K tiles reach double-buffered LDS through 16-byte
+// global->LDS copies issued by group 0 before its VALU phase.  Sweep 1 keeps
+// each query's running max and sum, sweep 2 the block sums, with the same
+// arithmetic in the same order as energy_kernel (the results are the same
+// bits).
+template <int D>
+__global__ __launch_bounds__(512) void energy_pp_kernel(const __bf16* __restrict__ q,
+                                                        const __bf16* __restrict__ k, int N, int nB,
+                                                        float c2, double* __restrict__ E) {
+  energy_pair<D>(q, k, N, nB, c2, E, blockIdx.x, blockIdx.y);
 }
 
 // ---- row-repetitive heads ([CalibAtt] section 3.2) --------------------------
@@ -344,8 +523,12 @@ template <int D, int BLK>
 void launch_energy_t(const __bf16* q, const __bf16* k, const svg_shape& s, float scale, double* E,
                      hipStream_t st) {
   const int nB = ceil_div(s.N, BLK);
-  hipLaunchKernelGGL((energy_kernel<D, BLK>), dim3(nB, s.B * s.H), dim3(BLK * 2), 0, st, q, k, s.N, nB,
-                     scale * 1.4426950408889634f, E);
+  if constexpr (BLK == 128)
+    hipLaunchKernelGGL((energy_pp_kernel<D>), dim3((nB + 1) / 2, s.B * s.H), dim3(512), 0, st, q, k, s.N, nB,
+                       scale * 1.4426950408889634f, E);
+  else
+    hipLaunchKernelGGL((energy_kernel<D, BLK>), dim3(nB, s.B * s.H), dim3(BLK * 2), 0, st, q, k, s.N, nB,
+                       scale * 1.4426950408889634f, E);
 }
 
 }  // namespace
