@@ -165,23 +165,71 @@ __global__ __launch_bounds__(BLK * 2, 2) void energy_kernel(const __bf16* __rest
   if (tid == 0) finish(nB - 1);
 }
 
+// Row sums of a 32 x 128 tile held in MFMA accumulator layout (lane (n, h)
+// holds query n's scores of keys 32 kt + 8 (i/4) + 4 h + i%4 in v[16 kt + i]):
+// a reduce-scatter over the 32 lanes of each half.  The first step swaps
+// 16-lane rows between registers (v_permlane16_swap), the next four pair
+// lanes by DPP (mirror of 16, mirror of 8, quad xor 2, quad xor 1); at each
+// step a lane keeps one of two value sets and adds its partner's copy.  Lane
+// (n, h) ends with the sums over the 32 queries of values 2n and 2n + 1, i.e.
+// keys 32 (n/8) + 8 ((n%8)/2) + 4 h + 2 (n%2) + {0, 1}.
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {
+  // the s_nops cover the VALU -> permlane and permlane -> VALU operand hazards
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int HALF, int CTRL>
+__device__ __forceinline__ void fold(float* v, bool upper) {
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
+    const float send = upper ? v[j] : v[j + HALF];
+    const float keep = upper ? v[j + HALF] : v[j];
+    v[j] = keep + dpp_f<CTRL>(send);
+  }
+}
+__device__ __forceinline__ void key_sums32(float* v, int n) {
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    float a = v[j], b = v[j + 32];
+    swap_rows16(a, b);
+    v[j] = a + b;
+  }
+  fold<16, 0x140>(v, n & 8);   // row_mirror: lane ^ 15
+  fold<8, 0x141>(v, n & 4);    // row_half_mirror: lane ^ 7
+  fold<4, 0x4E>(v, n & 2);     // quad_perm [2, 3, 0, 1]
+  fold<2, 0xB1>(v, n & 1);     // quad_perm [1, 0, 3, 2]
+}
+
+// Where sweep 2's sums go: block energies E [bh][nB][nB] (float64), or, for
+// the row-repetition test, the key-level pattern A [bh][rows][N] (fp32) of
+// latent rows of Ws queries.
+struct PairOut {
+  double* E;
+  float* A;
+  int Ws, rows;
+};
+
 // 128-token blocks: the attention kernel's two-phase schedule.  One
-// workgroup of 8 wavefronts takes two query blocks of a head (rows 2p and
-// 2p + 1 of E): group 0 (waves 0-3) computes S^T of key block j on the
+// workgroup of 8 wavefronts takes two query sets of a head (two query blocks,
+// or two latent rows): group 0 (waves 0-3) computes S^T of key block j on the
 // matrix cores while group 1 works on block j-1's scores on the VALU, then
 // the roles swap; K tiles reach double-buffered LDS through 16-byte
 // global->LDS copies issued by group 0 before its VALU phase.  Sweep 1 keeps
-// each query's running max and sum, sweep 2 the block sums, with the same
-// arithmetic in the same order as energy_kernel (the results are the same
-// bits).
-template <int D>
-__device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const __bf16* __restrict__ k, int N,
-                                            int nB, float c2, double* __restrict__ E, int pair, int bh) {
+// each query's running max and sum; sweep 2 sums exp2(s - lse) per key block
+// (energies: the same arithmetic in the same order as energy_kernel, so the
+// same bits) or per key (row patterns: key_sums32 over a wave's 32 queries,
+// then the four waves added in order).
+template <int D, bool ROWS>
+__device__ __forceinline__ void pair_sweeps(const __bf16* __restrict__ q, const __bf16* __restrict__ k, int N,
+                                            int nB, float c2, PairOut out, int pair, int bh) {
   using C = Cfg2<D>;
   // separate arrays per buffer, addressed with compile-time indices (the
   // compiler then sees that copies in flight target the other buffer)
   __shared__ uint4 kbuf0[C::KBYTES / 16], kbuf1[C::KBYTES / 16];
-  __shared__ float part[2][2][4];   // [block parity][group][wave]
+  __shared__ float part[2][2][ROWS ? 4 * 128 : 4];   // [block parity][group][wave (x key)]
   char* const kb_lds[2] = {reinterpret_cast<char*>(kbuf0), reinterpret_cast<char*>(kbuf1)};
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
@@ -189,12 +237,20 @@ __device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const 
   const int grp = wave >> 2;
   const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);
   const int n = lane & 31, h = lane >> 5;
-  const int qb = 2 * pair + grp;
-  const bool has_row = qb < nB;
+  const int unit = 2 * pair + grp;   // query block, or latent row
   const __bf16* qh = q + int64_t(bh) * N * D;
   const char* Kh = reinterpret_cast<const char*>(k + int64_t(bh) * N * D);
-  const int qi = qb * 128 + w4 * 32 + n;
-  const bool q_ok = qi < N;
+  bool has_unit, q_ok;
+  int qi;
+  if constexpr (ROWS) {
+    has_unit = unit < out.rows;
+    q_ok = has_unit && w4 * 32 + n < out.Ws;
+    qi = unit * out.Ws + w4 * 32 + n;
+  } else {
+    has_unit = unit < nB;
+    qi = unit * 128 + w4 * 32 + n;
+    q_ok = qi < N;
+  }
   bf16x8 qreg[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
@@ -223,7 +279,7 @@ __device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const 
   auto key_of = [&](int kb, int kt, int i) { return kb * 128 + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3); };
 
   float m = -INFINITY, l = 0.f, lse2 = 0.f;
-  // sweep 1: running max and sum; sweep 2: block sums of exp2(s - lse)
+  // sweep 1: running max and sum; sweep 2: sums of exp2(s - lse)
   auto stats = [&](int kb) {
     if (kb * 128 + 128 > N) {   // the ragged last block: keys past N drop out
 #pragma unroll
@@ -248,27 +304,39 @@ __device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const 
     m = m_new;
   };
   auto bsum = [&](int kb) {
-    float sum = 0.f;
-    if (kb * 128 + 128 > N) {
+    if constexpr (ROWS) {
+      // queries outside the row have lse2 = +inf, so their weights are 0;
+      // keys past N are summed but never stored
+      float v[64];
 #pragma unroll
       for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
-          sum += key_of(kb, kt, i) < N ? p : 0.f;
-        }
+        for (int i = 0; i < 16; ++i) v[16 * kt + i] = fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+      key_sums32(v, n);
+      const int key0 = 32 * (n >> 3) + 8 * ((n & 7) >> 1) + 4 * h + 2 * (n & 1);
+      *reinterpret_cast<float2*>(&part[kb & 1][grp][w4 * 128 + key0]) = make_float2(v[0], v[1]);
     } else {
+      float sum = 0.f;
+      if (kb * 128 + 128 > N) {
 #pragma unroll
-      for (int kt = 0; kt < C::KT; ++kt)
+        for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+          for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+            sum += key_of(kb, kt, i) < N ? p : 0.f;
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
+      }
+      if (!q_ok) sum = 0.f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      if (lane == 0) part[kb & 1][grp][w4] = sum;   // summed after the iteration's barrier
     }
-    if (!q_ok) sum = 0.f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if (lane == 0) part[kb & 1][grp][w4] = sum;   // summed after the iteration's barrier
   };
-  double* erow = E + (int64_t(bh) * nB + qb) * nB;
   // iteration j: K of block j in buffer j % 2; group 1 handles block j-1's
   // scores in phase 1, group 0 block j's in phase 2
   auto iteration = [&](int j, auto kbuf_c, auto second_c) {
@@ -299,13 +367,21 @@ __device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const 
     if constexpr (SECOND) {
       // group 0's block j and group 1's block j-1 are complete: four wave
       // sums each, added in wave order
-      if ((tid & 255) == 0) {
-        const int kbd = grp == 0 ? j : j - 1;
-        if (kbd >= 0 && kbd < nB && has_row) {
+      const int kbd = grp == 0 ? j : j - 1;
+      if constexpr (ROWS) {
+        const int key = tid & 255;
+        if (key < 128 && kbd >= 0 && kbd < nB && has_unit && kbd * 128 + key < N) {
+          float t = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) t += part[kbd & 1][grp][w * 128 + key];
+          out.A[(int64_t(bh) * out.rows + unit) * N + kbd * 128 + key] = t;
+        }
+      } else if ((tid & 255) == 0) {
+        if (kbd >= 0 && kbd < nB && has_unit) {
           float t = 0.f;
 #pragma unroll
           for (int w = 0; w < 4; ++w) t += part[kbd & 1][grp][w];
-          erow[kbd] = double(t);
+          out.E[(int64_t(bh) * nB + unit) * nB + kbd] = double(t);
         }
       }
     }
@@ -321,24 +397,18 @@ __device__ __forceinline__ void energy_pair(const __bf16* __restrict__ q, const 
   };
   sweep(std::false_type{});
   lse2 = m + __log2f(l + __shfl_xor(l, 32, 64));
+  if constexpr (ROWS) {
+    if (!q_ok) lse2 = INFINITY;
+  }
   barrier_lds();   // every wave is done with the tiles of sweep 1
   sweep(std::true_type{});
 }
 
-// 128-token blocks: the attention kernel's two-phase schedule.  One
-// workgroup of 8 wavefronts takes two query blocks of a head (rows 2p and
-// 2p + 1 of E): group 0 (waves 0-3) computes S^T of key block j on the
-// matrix cores while group 1 works on block j-1's scores on the VALU, then
-// the roles swap; K tiles reach double-buffered LDS through 16-byte
-// global->LDS copies issued by group 0 before its VALU phase.  Sweep 1 keeps
-// each query's running max and sum, sweep 2 the block sums, with the same
-// arithmetic in the same order as energy_kernel (the results are the same
-// bits).
 template <int D>
 __global__ __launch_bounds__(512) void energy_pp_kernel(const __bf16* __restrict__ q,
                                                         const __bf16* __restrict__ k, int N, int nB,
                                                         float c2, double* __restrict__ E) {
-  energy_pair<D>(q, k, N, nB, c2, E, blockIdx.x, blockIdx.y);
+  pair_sweeps<D, false>(q, k, N, nB, c2, PairOut{E, nullptr, 0, 0}, blockIdx.x, blockIdx.y);
 }
 
 // ---- row-repetitive heads ([CalibAtt] section 3.2) --------------------------
@@ -346,103 +416,14 @@ __global__ __launch_bounds__(512) void energy_pp_kernel(const __bf16* __restrict
 // of its Ws queries over all N keys; a head is row-repetitive when the mean
 // cosine between the patterns of the rows of a frame exceeds gamma.
 //
-// row_pattern_kernel: one workgroup per (batch*head, latent row), four
-// wavefronts of 32 query slots (Ws <= 128; slots past Ws masked).  Sweep 1 is
-// the energy kernel's (running max and sum per query, K tiles double-buffered
-// in LDS, the second tile borrowing the weight buffer); sweep 2 writes each
-// 128-key block's weights to an LDS buffer [query][key] and 128 threads sum a
-// key's column over the queries in order.  fp32 sums, identical on every call.
-constexpr int kPRS = 128 * 4 + 16;   // weight-buffer row stride (bytes): one query, 128 keys
-
+// row_pattern_kernel: pair_sweeps with latent rows as the query sets, two
+// rows of a head per workgroup (Ws <= 128; slots past Ws have zero weight).
+// fp32 sums in a fixed order, identical on every call.
 template <int D>
-__global__ __launch_bounds__(256) void row_pattern_kernel(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(512) void row_pattern_kernel(const __bf16* __restrict__ q,
                                                           const __bf16* __restrict__ k, int N, int Ws,
                                                           int rows, float c2, float* __restrict__ A) {
-  using C = ECfg<D, 128>;
-  static_assert(C::THREADS == 256, "four wavefronts");
-  __shared__ __attribute__((aligned(16))) char ktile[128 * C::RS];
-  __shared__ __attribute__((aligned(16))) char pbuf[128 * kPRS];
-  static_assert(128 * kPRS >= 128 * C::RS, "the weight buffer holds a K tile in sweep 1");
-  const int row = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 31, h = lane >> 5;
-  const int nB = (N + 127) / 128;
-  const __bf16* qh = q + int64_t(bh) * N * D;
-  const __bf16* kh = k + int64_t(bh) * N * D;
-  const int slot = wave * 32 + n;
-  const bool q_ok = slot < Ws;
-  const int qi = row * Ws + slot;
-  bf16x8 qreg[C::DK];
-#pragma unroll
-  for (int kk = 0; kk < C::DK; ++kk) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (q_ok) u = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * kk + 8 * h);
-    qreg[kk] = as_bf16x8(u);
-  }
-  f32x16 sacc[C::KT];
-  auto key_of = [&](int kb, int kt, int i) { return kb * 128 + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3); };
-  uint4 kr[C::LOADS];
-
-  float m = -INFINITY, l = 0.f;
-  load_k<D, 128>(kr, kh, 0, N, tid);
-  for (int kb = 0; kb < nB; ++kb) {
-    char* tile = (kb & 1) ? pbuf : ktile;
-    store_k<D, 128>(tile, kr, tid);
-    __syncthreads();
-    if (kb + 1 < nB) load_k<D, 128>(kr, kh, kb + 1, N, tid);
-    scores<D, 128>(tile, qreg, n, h, sacc);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (key_of(kb, kt, i) >= N) sacc[kt][i] = -INFINITY;
-        mx = fmaxf(mx, sacc[kt][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    const float m_new = fmaxf(m, mx);
-    float add = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) add += fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -m_new));
-    l = l * fast_exp2(m - m_new) + add;
-    m = m_new;
-  }
-  const float lse2 = m + __log2f(l + __shfl_xor(l, 32, 64));
-
-  float* arow = A + (int64_t(bh) * rows + row) * N;
-  __syncthreads();   // sweep 1's tiles are no longer read
-  load_k<D, 128>(kr, kh, 0, N, tid);
-  for (int kb = 0; kb < nB; ++kb) {
-    store_k<D, 128>(ktile, kr, tid);   // the tile and the weights of block kb-1 are no longer read
-    __syncthreads();
-    if (kb + 1 < nB) load_k<D, 128>(kr, kh, kb + 1, N, tid);
-    scores<D, 128>(ktile, qreg, n, h, sacc);
-    char* prow = pbuf + slot * kPRS;
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float4 w;
-        float* wp = reinterpret_cast<float*>(&w);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g4 + j;
-          const float p = fast_exp2(__builtin_fmaf(sacc[kt][i], c2, -lse2));
-          wp[j] = (q_ok && key_of(kb, kt, i) < N) ? p : 0.f;
-        }
-        // keys kt*32 + 8*g4 + 4*h + 0..3 of the block
-        *reinterpret_cast<float4*>(prow + (kt * 32 + 8 * g4 + 4 * h) * 4) = w;
-      }
-    __syncthreads();
-    if (tid < 128 && kb * 128 + tid < N) {
-      float t = 0.f;
-      for (int r = 0; r < 128; ++r) t += *reinterpret_cast<const float*>(pbuf + r * kPRS + tid * 4);
-      arow[kb * 128 + tid] = t;
-    }
-    __syncthreads();
-  }
+  pair_sweeps<D, true>(q, k, N, (N + 127) / 128, c2, PairOut{nullptr, A, Ws, rows}, blockIdx.x, blockIdx.y);
 }
 
 // Per (batch*head, frame): Gram matrix of the frame's Hs row patterns (float64
@@ -562,9 +543,11 @@ void launch_row_similarity(const void* q, const void* k, const svg_shape& s, flo
   const __bf16* qb = static_cast<const __bf16*>(q);
   const __bf16* kb = static_cast<const __bf16*>(k);
   if (s.D == 128)
-    hipLaunchKernelGGL(row_pattern_kernel<128>, dim3(rows, heads), dim3(256), 0, st, qb, kb, s.N, s.Ws, rows, c2, A);
+    hipLaunchKernelGGL(row_pattern_kernel<128>, dim3((rows + 1) / 2, heads), dim3(512), 0, st, qb, kb, s.N, s.Ws,
+                       rows, c2, A);
   else
-    hipLaunchKernelGGL(row_pattern_kernel<64>, dim3(rows, heads), dim3(256), 0, st, qb, kb, s.N, s.Ws, rows, c2, A);
+    hipLaunchKernelGGL(row_pattern_kernel<64>, dim3((rows + 1) / 2, heads), dim3(512), 0, st, qb, kb, s.N, s.Ws,
+                       rows, c2, A);
   hipLaunchKernelGGL(row_gram_kernel, dim3(s.F, heads), dim3(256), 0, st, A, s.N, s.Hs, s.F, fsum);
   hipLaunchKernelGGL(row_score_kernel, dim3((heads + 255) / 256), dim3(256), 0, st, fsum, s.F, s.Hs, heads, score);
 }
