@@ -532,6 +532,8 @@ svg_status svg_row_similarity(const void* q, const void* k, svg_shape s, float s
   if (!(scale > 0.f)) return fail(SVG_ERR_INVALID_ARG, "%s: scale must be positive", fn);
   if (s.Ws > 128 || s.Hs < 2 || s.Hs > 64)
     return fail(SVG_ERR_UNSUPPORTED, "%s: needs Ws <= 128 and 2 <= Hs <= 64", fn);
+  if (int64_t(s.Hs) * s.N * 4 >= (int64_t(1) << 31))
+    return fail(SVG_ERR_UNSUPPORTED, "%s: a frame's row patterns (Hs * N * 4 bytes) must stay under 2 GiB", fn);
   if (int64_t(s.B) * s.H > 65535) return fail(SVG_ERR_UNSUPPORTED, "%s: more than 65535 heads", fn);
   const size_t need = row_similarity_workspace_bytes(s);
   if (!workspace || workspace_bytes < need)

@@ -426,53 +426,120 @@ __global__ __launch_bounds__(512) void row_pattern_kernel(const __bf16* __restri
   pair_sweeps<D, true>(q, k, N, (N + 127) / 128, c2, PairOut{nullptr, A, Ws, rows}, blockIdx.x, blockIdx.y);
 }
 
-// Per (batch*head, frame): Gram matrix of the frame's Hs row patterns (float64
-// accumulation over the keys, 64 keys at a time through LDS), then the sum of
-// the cosines over the pairs of distinct rows, in order.
+// Per (batch*head, frame): Gram matrix G = P P^T of the frame's Hs row
+// patterns (P: Hs x N), a dense float64 contraction over the keys on the
+// matrix cores (v_mfma_f64_16x16x4_f64), split over key chunks to fill the
+// chip, then the sum of the cosines over the pairs of distinct rows, in order.
+// The fp32 pattern values convert exactly to float64, so every product is
+// exact and only the float64 accumulation rounds.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxHs = 64;
-__global__ __launch_bounds__(256) void row_gram_kernel(const float* __restrict__ A, int N, int Hs, int F,
-                                                       double* __restrict__ fsum) {
-  __shared__ float tile[kMaxHs][64 + 1];
-  __shared__ double gram[kMaxHs * (kMaxHs + 1) / 2];
-  const int f = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int pairs = Hs * (Hs + 1) / 2;   // (y <= z), packed row-major over y
+constexpr int kGramWaves = 4;
+
+// Key chunks per frame: enough workgroups for the 256 compute units, chunks a
+// multiple of 128 keys (4 wavefronts x 32 keys per step).
+struct GramSplit {
+  int chunks, chunk_keys;
+};
+GramSplit gram_split(const svg_shape& s) {
+  const int64_t frames = int64_t(s.B) * s.H * s.F;
+  const int max_chunks = (s.N + 127) / 128;
+  int chunks = int(std::min<int64_t>(max_chunks, std::max<int64_t>(1, (2048 + frames - 1) / frames)));
+  const int chunk_keys = ((s.N + chunks - 1) / chunks + 127) / 128 * 128;
+  chunks = (s.N + chunk_keys - 1) / chunk_keys;
+  return {chunks, chunk_keys};
+}
+constexpr int gram_tile_pairs(int rt) { return rt * (rt + 1) / 2; }
+
+// One workgroup per (frame, key chunk, batch*head); wave w takes the keys
+// k0 = chunk start + 32 w + 128 it.  Lane l carries row 16 t + l%16 of row
+// tile t and, at step s of a 32-key group, key k0 + 4 s + l/16: the same
+// register is the A operand (rows x keys) and the B operand (keys x rows), so
+// tile pair (ti, tj) accumulates G[16 ti + i][16 tj + j] for ti <= tj.  Each
+// wave writes its partial tiles, [16 x 16] row-major per pair.
+template <int RT>
+__global__ __launch_bounds__(256) void row_gram_part_kernel(const float* __restrict__ A, int N, int Hs, int F,
+                                                            int chunks, int chunk_keys,
+                                                            double* __restrict__ part) {
+  constexpr int NP = gram_tile_pairs(RT);
+  const int f = blockIdx.x / chunks, c = blockIdx.x % chunks, bh = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
   const float* base = A + (int64_t(bh) * F + f) * Hs * int64_t(N);
-  constexpr int PPT = (kMaxHs * (kMaxHs + 1) / 2 + 255) / 256;
-  double acc[PPT];
-  int py[PPT], pz[PPT];
+  const int kbeg = c * chunk_keys, kend = min(N, kbeg + chunk_keys);
+  // the frame's patterns as a buffer resource: reads at offsets past its end
+  // return 0, which pads the rows past Hs and the keys past the chunk
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, Hs * N * 4, 0x00020000);
+#endif
+  uint32_t row_off[RT];
 #pragma unroll
-  for (int u = 0; u < PPT; ++u) {
-    acc[u] = 0.0;
-    int p = tid + u * 256, y = 0;
-    while (p >= Hs - y && y < Hs) { p -= Hs - y; ++y; }
-    py[u] = y;
-    pz[u] = y + p;
+  for (int t = 0; t < RT; ++t) {
+    const int row = 16 * t + r16;
+    row_off[t] = row < Hs ? uint32_t(row) * uint32_t(N) * 4u : 0x80000000u;
   }
-  for (int j0 = 0; j0 < N; j0 += 64) {
-    __syncthreads();
-    for (int e = tid; e < Hs * 64; e += 256) {
-      const int y = e / 64, j = e % 64;
-      tile[y][j] = j0 + j < N ? base[int64_t(y) * N + j0 + j] : 0.f;
-    }
-    __syncthreads();
+  f64x4 acc[NP];
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      if (tid + u * 256 < pairs) {
-        double s = 0.0;
-        for (int j = 0; j < 64; ++j) s += double(tile[py[u]][j]) * double(tile[pz[u]][j]);
-        acc[u] += s;
+  for (int p = 0; p < NP; ++p) acc[p] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = kbeg + 32 * wave; k0 < kend; k0 += 32 * kGramWaves) {
+    float x[RT][8];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int key = k0 + 4 * s + g;
+        const uint32_t off = key < kend ? row_off[t] + uint32_t(key) * 4u : 0x80000000u;
+#if defined(__HIP_DEVICE_COMPILE__)
+        x[t][s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+#else
+        x[t][s] = float(off);
+#endif
       }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      double a[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) a[t] = double(x[t][s]);
+      int p = 0;
+#pragma unroll
+      for (int ti = 0; ti < RT; ++ti)
+#pragma unroll
+        for (int tj = ti; tj < RT; ++tj, ++p) acc[p] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ti], a[tj], acc[p], 0, 0, 0);
     }
   }
+  // accumulator layout of the float64 product (unlike the fp32 ones): register
+  // r of lane l holds row l/16 + 4 r, column l%16
+  double* dst = part + (((int64_t(bh) * F + f) * chunks + c) * kGramWaves + wave) * NP * 256;
 #pragma unroll
-  for (int u = 0; u < PPT; ++u)
-    if (tid + u * 256 < pairs) gram[tid + u * 256] = acc[u];
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[p * 256 + (g + 4 * r) * 16 + r16] = acc[p][r];
+}
+
+// Per (frame, batch*head): the partial tiles added in (chunk, wave) order,
+// then the cosine sum over the pairs y < z in order.
+template <int RT>
+__global__ __launch_bounds__(256) void row_gram_sum_kernel(const double* __restrict__ part, int Hs, int F,
+                                                           int chunks, double* __restrict__ fsum) {
+  constexpr int NP = gram_tile_pairs(RT);
+  __shared__ double gram[16 * RT][16 * RT + 1];
+  const int f = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int parts = chunks * kGramWaves;
+  const double* src = part + (int64_t(bh) * F + f) * parts * NP * 256;
+  for (int e = tid; e < NP * 256; e += 256) {
+    double t = 0.0;
+    for (int u = 0; u < parts; ++u) t += src[int64_t(u) * NP * 256 + e];
+    int p = e / 256, ti = 0;
+    while (p >= RT - ti) { p -= RT - ti; ++ti; }
+    const int tj = ti + p;
+    gram[16 * ti + (e % 256) / 16][16 * tj + e % 16] = t;
+  }
   __syncthreads();
   if (tid == 0) {
-    auto at = [&](int y, int z) { return gram[y * Hs - y * (y - 1) / 2 + (z - y)]; };
     double total = 0.0;
     for (int y = 0; y < Hs; ++y)
-      for (int z = y + 1; z < Hs; ++z) total += at(y, z) / sqrt(at(y, y) * at(z, z));
+      for (int z = y + 1; z < Hs; ++z) total += gram[y][z] / sqrt(gram[y][y] * gram[z][z]);
     fsum[int64_t(bh) * F + f] = total;
   }
 }
@@ -529,16 +596,31 @@ void launch_block_energy(const void* q, const void* k, const svg_shape& s, float
 
 size_t row_similarity_workspace_bytes(const svg_shape& s) {
   const int64_t heads = int64_t(s.B) * s.H;
-  const int64_t a_bytes = heads * s.F * s.Hs * int64_t(s.N) * 4;
-  return size_t((a_bytes + 255) / 256 * 256 + heads * s.F * 8);
+  const int64_t a_bytes = (heads * s.F * s.Hs * int64_t(s.N) * 4 + 255) / 256 * 256;
+  const int64_t f_bytes = (heads * s.F * 8 + 255) / 256 * 256;
+  const GramSplit sp = gram_split(s);
+  const int rt = (s.Hs + 15) / 16;
+  const int64_t p_bytes = heads * s.F * sp.chunks * kGramWaves * gram_tile_pairs(rt) * 256 * 8;
+  return size_t(a_bytes + f_bytes + p_bytes);
+}
+
+template <int RT>
+void launch_gram(const float* A, const svg_shape& s, const GramSplit& sp, double* part, double* fsum,
+                 hipStream_t st) {
+  const int heads = s.B * s.H;
+  hipLaunchKernelGGL(row_gram_part_kernel<RT>, dim3(s.F * sp.chunks, heads), dim3(256), 0, st, A, s.N, s.Hs, s.F,
+                     sp.chunks, sp.chunk_keys, part);
+  hipLaunchKernelGGL(row_gram_sum_kernel<RT>, dim3(s.F, heads), dim3(256), 0, st, part, s.Hs, s.F, sp.chunks, fsum);
 }
 
 void launch_row_similarity(const void* q, const void* k, const svg_shape& s, float scale, double* score,
                            void* ws, hipStream_t st) {
   const int heads = s.B * s.H, rows = s.F * s.Hs;
   float* A = static_cast<float*>(ws);
-  const int64_t a_bytes = int64_t(heads) * rows * int64_t(s.N) * 4;
-  double* fsum = reinterpret_cast<double*>(static_cast<char*>(ws) + (a_bytes + 255) / 256 * 256);
+  const int64_t a_bytes = (int64_t(heads) * rows * int64_t(s.N) * 4 + 255) / 256 * 256;
+  const int64_t f_bytes = (int64_t(heads) * s.F * 8 + 255) / 256 * 256;
+  double* fsum = reinterpret_cast<double*>(static_cast<char*>(ws) + a_bytes);
+  double* part = reinterpret_cast<double*>(static_cast<char*>(ws) + a_bytes + f_bytes);
   const float c2 = scale * 1.4426950408889634f;
   const __bf16* qb = static_cast<const __bf16*>(q);
   const __bf16* kb = static_cast<const __bf16*>(k);
@@ -548,7 +630,13 @@ void launch_row_similarity(const void* q, const void* k, const svg_shape& s, flo
   else
     hipLaunchKernelGGL(row_pattern_kernel<64>, dim3((rows + 1) / 2, heads), dim3(512), 0, st, qb, kb, s.N, s.Ws,
                        rows, c2, A);
-  hipLaunchKernelGGL(row_gram_kernel, dim3(s.F, heads), dim3(256), 0, st, A, s.N, s.Hs, s.F, fsum);
+  const GramSplit sp = gram_split(s);
+  switch ((s.Hs + 15) / 16) {
+    case 1: launch_gram<1>(A, s, sp, part, fsum, st); break;
+    case 2: launch_gram<2>(A, s, sp, part, fsum, st); break;
+    case 3: launch_gram<3>(A, s, sp, part, fsum, st); break;
+    default: launch_gram<4>(A, s, sp, part, fsum, st); break;
+  }
   hipLaunchKernelGGL(row_score_kernel, dim3((heads + 255) / 256), dim3(256), 0, st, fsum, s.F, s.Hs, heads, score);
 }
 

@@ -348,10 +348,12 @@ svg_status svg_aggregate_masks(const uint8_t* masks, int n_sets, int64_t mask_el
  *   score     : device double [B*H] out.
  *   workspace : device, >= svg_row_similarity_workspace_bytes(s) bytes,
  *               256-byte aligned: the row patterns, float [B*H][F*Hs][N],
- *               then per-frame sums (Wan 720p: 286 MB per head).
- * fp32 weights and pattern sums, float64 Gram sums, fixed order (identical on
- * every call).  SVG_ERR_UNSUPPORTED for Ws > 128, Hs outside [2, 64], D
- * outside {64, 128} or B*H > 65535; SVG_ERR_CAPACITY for a short workspace. */
+ *               then per-frame sums and partial Gram tiles (Wan 720p: 289 MB
+ *               per head).
+ * fp32 weights and pattern sums, float64 Gram sums (exact products), fixed
+ * order (identical on every call).  SVG_ERR_UNSUPPORTED for Ws > 128, Hs
+ * outside [2, 64], Hs * N * 4 >= 2^31, D outside {64, 128} or B*H > 65535;
+ * SVG_ERR_CAPACITY for a short workspace. */
 size_t svg_row_similarity_workspace_bytes(svg_shape s);
 svg_status svg_row_similarity(const void* q, const void* k, svg_shape s, float scale, double* score,
                               void* workspace, size_t workspace_bytes, void* stream);

@@ -228,6 +228,7 @@ def test_calibration_validation():
     assert lib.svg_row_similarity(FAKE, FAKE, _shape(Ws=256, N=4 * 16 * 256), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
     assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=1, Ws=256, N=1024), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
     assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=65, Ws=4, N=1040), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
+    assert lib.svg_row_similarity(FAKE, FAKE, _shape(Hs=64, Ws=1, N=1 << 23), 0.1, FAKE2, big, 1 << 40, None) == L.SVG_ERR_UNSUPPORTED
 
 
 def test_qk_norm_rope_validation():
