@@ -17,28 +17,47 @@ __global__ void fp8_zero_kernel(uint32_t* amax, int n) {
   if (i < n) amax[i] = 0u;
 }
 
-// max |x| of one (tensor, head): blockIdx.y = head, blockIdx.z = tensor
-// (q, k, v); the float bits of non-negative values order like the values, so
-// an unsigned atomic max combines the workgroups.
+constexpr int kAmaxChunks = 4096;   // 16-byte chunks per amax step of a workgroup (64 KB)
+constexpr int kAmaxGroups = 32;     // workgroups per (tensor, head)
+
+// max |x| of one (tensor, head): blockIdx.y = head, blockIdx.z = tensor.
+// Workgroup x reads its contiguous share of the head in steps of 64 KB (16
+// loads per thread in flight); its maximum goes to the result with one
+// unsigned atomic max (the float bits of non-negative values order like the
+// values), so that few atomics meet on one address.
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                        const uint4* __restrict__ v, int64_t chunks_per_head,
                                                        uint32_t* __restrict__ amax, int BH) {
   const int bh = blockIdx.y, t = blockIdx.z;
   const uint4* x = (t == 0 ? q : t == 1 ? k : v) + int64_t(bh) * chunks_per_head;
+  const int64_t span = (chunks_per_head + gridDim.x - 1) / gridDim.x;
+  const int64_t begin = int64_t(blockIdx.x) * span, end = min(chunks_per_head, begin + span);
   uint32_t m = 0u;
-  for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < chunks_per_head; c += int64_t(gridDim.x) * 256) {
-    const uint4 u = x[c];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int64_t c0 = begin + threadIdx.x; c0 < end; c0 += kAmaxChunks) {
+    // indices past the share re-read its last chunk, which leaves the maximum unchanged
+    uint4 u[kAmaxChunks / 256];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // |bf16| bits widened to fp32 bits: the order of the values is kept
-      m = max(m, (w[j] & 0x7fffu) << 16);
-      m = max(m, w[j] & 0x7fff0000u);
+    for (int r = 0; r < kAmaxChunks / 256; ++r) u[r] = x[min(c0 + r * 256, end - 1)];
+#pragma unroll
+    for (int r = 0; r < kAmaxChunks / 256; ++r) {
+      const uint32_t w[4] = {u[r].x, u[r].y, u[r].z, u[r].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // |bf16| bits widened to fp32 bits: the order of the values is kept
+        m = max(m, (w[j] & 0x7fffu) << 16);
+        m = max(m, w[j] & 0x7fff0000u);
+      }
     }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), off, 64)));
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(amax + t * BH + bh, m);
+  __shared__ uint32_t wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (m) atomicMax(amax + t * BH + bh, m);
+  }
 }
 
 __device__ __forceinline__ float inv_scale(uint32_t amax_bits) {
@@ -81,45 +100,73 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const __bf16* __restrict
   const uint4* vs = reinterpret_cast<const uint4*>(v + off);
   uint2* qd = reinterpret_cast<uint2*>(q8 + off);
   uint2* kd = reinterpret_cast<uint2*>(k8 + off);
-  // Q rows (frame-major) and K rows (row r of the head's layout <- k[fm(r)])
+  // Q rows (frame-major) and K rows (row r of the head's layout <- k[fm(r)]):
+  // every load is issued before the first store (rows past N read row N-1
+  // and are not stored)
+  constexpr int U = BLK * CPR / 256;
+  uint4 qv[U], kv[U];
 #pragma unroll
-  for (int u = 0; u < BLK * CPR / 256; ++u) {
+  for (int u = 0; u < U; ++u) {
+    const int c = t + u * 256;
+    const int r = min(kb * BLK + c / CPR, N - 1), col = c % CPR;
+    const int src = tm ? frame_major_of(r, a) : r;
+    qv[u] = qs[int64_t(r) * CPR + col];
+    kv[u] = ks[int64_t(src) * CPR + col];
+  }
+  // V^T: thread (kg, dc) takes keys 8 kg .. 8 kg + 7 and dims 8 dc .. 8 dc + 7
+  // (loaded here, before the Q and K stores) and places them in an LDS tile
+  // of the block's V^T rows (one padding word per row); the tile then leaves
+  // as whole 128-byte rows
+  constexpr int TASKS = (BLK / 8) * CPR;
+  const int dc = t % CPR, kg = t / CPR;
+  uint4 vv[8];
+  if (t < TASKS) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = min(kb * BLK + 8 * kg + i, N - 1);
+      const int src = tm ? frame_major_of(key, a) : key;
+      vv[i] = vs[int64_t(src) * CPR + dc];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
     const int c = t + u * 256;
     const int r = kb * BLK + c / CPR, col = c % CPR;
     if (r < N) {
-      qd[int64_t(r) * CPR + col] = to_e4m3(qs[int64_t(r) * CPR + col], iq);
-      const int src = tm ? frame_major_of(r, a) : r;
-      kd[int64_t(r) * CPR + col] = to_e4m3(ks[int64_t(src) * CPR + col], ik);
+      qd[int64_t(r) * CPR + col] = to_e4m3(qv[u], iq);
+      kd[int64_t(r) * CPR + col] = to_e4m3(kv[u], ik);
     }
   }
-  // V^T: thread (kg, dc) takes keys 8 kg .. 8 kg + 7 and dims 8 dc .. 8 dc + 7
-  constexpr int TASKS = (BLK / 8) * CPR;
-  if (t >= TASKS) return;
-  const int dc = t % CPR, kg = t / CPR;
-  uint2 rows[8];
+  __shared__ uint32_t tile[D][BLK / 4 + 1];
+  if (t < TASKS) {
+    uint2 rows[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = kb * BLK + 8 * kg + i;
-    const int src = tm && key < N ? frame_major_of(key, a) : key;
-    rows[i] = key < N ? to_e4m3(vs[int64_t(src) * CPR + dc], iv) : make_uint2(0u, 0u);
+    for (int i = 0; i < 8; ++i)
+      rows[i] = kb * BLK + 8 * kg + i < N ? to_e4m3(vv[i], iv) : make_uint2(0u, 0u);
+    // byte j of rows[i] is (key 8 kg + i, dim 8 dc + j); keys i = 0..3 go to
+    // bytes 64 g + 4 (kg % 8) + i of the V^T row, keys 4..7 32 bytes further
+    const int w0 = 16 * (kg / 8) + (kg % 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t b0 = ((j < 4 ? rows[i].x : rows[i].y) >> (8 * (j & 3))) & 0xffu;
+        const uint32_t b1 = ((j < 4 ? rows[i + 4].x : rows[i + 4].y) >> (8 * (j & 3))) & 0xffu;
+        lo |= b0 << (8 * i);
+        hi |= b1 << (8 * i);
+      }
+      tile[8 * dc + j][w0] = lo;
+      tile[8 * dc + j][w0 + 8] = hi;
+    }
   }
-  // byte j of rows[i] is (key 8 kg + i, dim 8 dc + j); keys i = 0..3 go to
-  // bytes 64 g + 4 (kg % 8) + i of the V^T row, keys 4..7 32 bytes further
+  __syncthreads();
   uint8_t* blk = vt8 + (int64_t(bh) * a.n_kb + kb) * BLK * D;
-  const int pos0 = 64 * (kg / 8) + 4 * (kg % 8);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t b0 = ((j < 4 ? rows[i].x : rows[i].y) >> (8 * (j & 3))) & 0xffu;
-      const uint32_t b1 = ((j < 4 ? rows[i + 4].x : rows[i + 4].y) >> (8 * (j & 3))) & 0xffu;
-      lo |= b0 << (8 * i);
-      hi |= b1 << (8 * i);
-    }
-    uint8_t* row = blk + (8 * dc + j) * BLK;
-    *reinterpret_cast<uint32_t*>(row + pos0) = lo;
-    *reinterpret_cast<uint32_t*>(row + pos0 + 32) = hi;
+  for (int u = 0; u < D * 8 / 256; ++u) {
+    const int e = t + u * 256, r = e / 8, c = e % 8;
+    const uint4 w = make_uint4(tile[r][4 * c], tile[r][4 * c + 1], tile[r][4 * c + 2], tile[r][4 * c + 3]);
+    *reinterpret_cast<uint4*>(blk + r * BLK + 16 * c) = w;
   }
 }
 
@@ -139,7 +186,7 @@ void launch_quantize_fp8(const AttnArgs& a, const void* q, const void* k, const 
   const int n = 3 * a.BH;
   hipLaunchKernelGGL(fp8_zero_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, bits, n);
   const int64_t chunks = int64_t(a.N) * a.D / 8;
-  const int per_head = int(std::min<int64_t>(64, (chunks + 256 * 16 - 1) / (256 * 16)));
+  const int per_head = int(std::min<int64_t>(kAmaxGroups, (chunks + kAmaxChunks - 1) / kAmaxChunks));
   hipLaunchKernelGGL(fp8_amax_kernel, dim3(per_head, a.BH, 3), dim3(256), 0, st,
                      static_cast<const uint4*>(q), static_cast<const uint4*>(k), static_cast<const uint4*>(v),
                      chunks, bits, a.BH);
