@@ -17,8 +17,15 @@ __global__ void fp8_zero_kernel(uint32_t* amax, int n) {
   if (i < n) amax[i] = 0u;
 }
 
+// 16-byte load that does not keep the line in the caches: the inputs here
+// are read once per pass and would only evict other data
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 constexpr int kAmaxChunks = 4096;   // 16-byte chunks per amax step of a workgroup (64 KB)
-constexpr int kAmaxGroups = 32;     // workgroups per (tensor, head)
 
 // max |x| of one (tensor, head): blockIdx.y = head, blockIdx.z = tensor.
 // Workgroup x reads its contiguous share of the head in steps of 64 KB (16
@@ -37,7 +44,7 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint4* __restrict__
     // indices past the share re-read its last chunk, which leaves the maximum unchanged
     uint4 u[kAmaxChunks / 256];
 #pragma unroll
-    for (int r = 0; r < kAmaxChunks / 256; ++r) u[r] = x[min(c0 + r * 256, end - 1)];
+    for (int r = 0; r < kAmaxChunks / 256; ++r) u[r] = ld_stream(x + min(c0 + r * 256, end - 1));
 #pragma unroll
     for (int r = 0; r < kAmaxChunks / 256; ++r) {
       const uint32_t w[4] = {u[r].x, u[r].y, u[r].z, u[r].w};
@@ -110,8 +117,8 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const __bf16* __restrict
     const int c = t + u * 256;
     const int r = min(kb * BLK + c / CPR, N - 1), col = c % CPR;
     const int src = tm ? frame_major_of(r, a) : r;
-    qv[u] = qs[int64_t(r) * CPR + col];
-    kv[u] = ks[int64_t(src) * CPR + col];
+    qv[u] = ld_stream(qs + int64_t(r) * CPR + col);
+    kv[u] = ld_stream(ks + int64_t(src) * CPR + col);
   }
   // V^T: thread (kg, dc) takes keys 8 kg .. 8 kg + 7 and dims 8 dc .. 8 dc + 7
   // (loaded here, before the Q and K stores) and places them in an LDS tile
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(const __bf16* __restrict
     for (int i = 0; i < 8; ++i) {
       const int key = min(kb * BLK + 8 * kg + i, N - 1);
       const int src = tm ? frame_major_of(key, a) : key;
-      vv[i] = vs[int64_t(src) * CPR + dc];
+      vv[i] = ld_stream(vs + int64_t(src) * CPR + dc);
     }
   }
 #pragma unroll
@@ -186,7 +193,10 @@ void launch_quantize_fp8(const AttnArgs& a, const void* q, const void* k, const 
   const int n = 3 * a.BH;
   hipLaunchKernelGGL(fp8_zero_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, bits, n);
   const int64_t chunks = int64_t(a.N) * a.D / 8;
-  const int per_head = int(std::min<int64_t>(kAmaxGroups, (chunks + kAmaxChunks - 1) / kAmaxChunks));
+  // workgroups per (tensor, head): about 1024 in all, at least 8 each (fewer,
+  // longer streams read faster than many short ones), at most one per step
+  const int groups = int(std::min<int64_t>(64, std::max<int64_t>(8, (1024 + 3 * a.BH - 1) / (3 * a.BH))));
+  const int per_head = int(std::min<int64_t>(groups, (chunks + kAmaxChunks - 1) / kAmaxChunks));
   hipLaunchKernelGGL(fp8_amax_kernel, dim3(per_head, a.BH, 3), dim3(256), 0, st,
                      static_cast<const uint4*>(q), static_cast<const uint4*>(k), static_cast<const uint4*>(v),
                      chunks, bits, a.BH);
