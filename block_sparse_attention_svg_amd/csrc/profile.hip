@@ -15,10 +15,12 @@
 //   tiles of 64 stream through double-buffered, padded LDS by 16-byte
 //   global->LDS copies; S^T = K Q^T and U_c^T += V^T P_c^T run on
 //   v_mfma_f32_16x16x32_bf16, the V^T operand coming from transposing LDS
-//   reads, Z_c from one more MFMA with an all-ones operand.  Each class keeps
-//   its own running max; within a 32-key step the spatial admission is the
-//   same for all keys of a query, so only two classes are live per lane, and
-//   only their MFMAs are issued (the other two are parked in registers).
+//   reads, Z_c from one more MFMA with an all-ones operand.  Within a 32-key
+//   step the spatial admission is the same for all keys of a query, so only
+//   two classes are live per lane, and only their MFMAs are issued (the other
+//   two are parked in registers); the live pair shares one running max per
+//   query (weights relative to a common scale lose nothing in floating
+//   point, and the merge weighs every record by its own max).
 //   Writes (m_c, Z_c, U_c) per (chunk, sample, class).
 // Pass 2 (profile_merge_kernel): one workgroup per (batch*head, sample):
 //   merges the chunks in a fixed order and evaluates both errors.
@@ -81,6 +83,14 @@ __device__ __forceinline__ int token_major(int j, const Geo& g) {
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 0xffff in each 16-bit half whose bit of `bits` (bit k for the low half,
+// k + 1 for the high half) is set
+__device__ __forceinline__ uint32_t pair_mask(uint32_t bits, int k) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_sbfe(int(bits), k, 1)) & 0xffffu;
+  const uint32_t hi = uint32_t(__builtin_amdgcn_sbfe(int(bits), k + 1, 1)) << 16;
+  return lo | hi;
+}
 
 // Exchange two registers of the active lanes in place (no temporary: the
 // swapped values stay in their registers, so a rarely taken swap adds no
@@ -211,13 +221,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // one run of frames), so every step issues MFMAs for two classes only.
   f32x4 uL[2][C::DT], uP[2][C::DT];
   f32x4 zL[2], zP[2];
-  float mL[2], mP[2];
+  float mL = -INFINITY, mP = -INFINITY;   // running max of the live / parked pair (log2 units)
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     zL[c] = f32x4{};
     zP[c] = f32x4{};
-    mL[c] = -INFINITY;
-    mP[c] = -INFINITY;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       uL[c][dt] = f32x4{};
@@ -288,8 +296,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt) swap_lane(uL[c][dt], uP[c][dt]);
             swap_lane(zL[c], zP[c]);
-            swap_lane(mL[c], mP[c]);
           }
+          swap_lane(mL, mP);
           s_live = inS;
         }
       }
@@ -302,51 +310,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int nv = k_end - (key0 + half * 32 + 8 * grp);
         vbits = nv >= 8 ? 0xffu : nv <= 0 ? 0u : (1u << nv) - 1u;
       }
-      const uint32_t in_bits = adm & vbits, out_bits = ~adm & vbits;
+      const uint32_t in_bits = adm & vbits;
       float x[8];
-      bool inT[8], outT[8];
-      float m_in = -INFINITY, m_out = -INFINITY;   // this lane's max over T-kept / T-skipped keys
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        inT[i] = (in_bits >> i) & 1u;
-        outT[i] = (out_bits >> i) & 1u;
-        x[i] = s2[i >> 2][i & 3];
-        m_in = fmaxf(m_in, inT[i] ? x[i] : -INFINITY);
-        m_out = fmaxf(m_out, outT[i] ? x[i] : -INFINITY);
+      for (int i = 0; i < 8; ++i) x[i] = s2[i >> 2][i & 3];
+      if (vbits != 0xffu) {   // keys past the chunk: weight 0, no part in the max
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (vbits >> i) & 1u ? x[i] : -INFINITY;
       }
-      m_in *= c2;
-      m_out *= c2;
+      // this lane's block max over its keys, for both live classes
+      float m_blk = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m_blk = fmaxf(m_blk, x[i]);
+      m_blk *= c2;
       // Fast path: no lane's block max exceeds its running max by more than
-      // 2^24, so the stale maxima stay valid and no cross-lane exchange is
+      // 2^24, so the stale maximum stays valid and no cross-lane exchange is
       // needed.  Otherwise combine the maxima over the 4 lanes of each sample
-      // and rescale the live classes whose maximum moved.
-      if (__ballot(m_in > mL[0] + kRescaleLog2 || m_out > mL[1] + kRescaleLog2)) {
-        m_in = fmaxf(m_in, shfl_xor_f(m_in, 16));
-        m_in = fmaxf(m_in, shfl_xor_f(m_in, 32));
-        m_out = fmaxf(m_out, shfl_xor_f(m_out, 16));
-        m_out = fmaxf(m_out, shfl_xor_f(m_out, 32));
-        const bool up_in = m_in > mL[0] + kRescaleLog2;
-        const bool up_out = m_out > mL[1] + kRescaleLog2;
-        const float f0 = up_in ? fast_exp2(mL[0] - m_in) : 1.f;
-        const float f1 = up_out ? fast_exp2(mL[1] - m_out) : 1.f;
-        zL[0] *= f0;
-        zL[1] *= f1;
+      // and rescale the live pair where its maximum moved.
+      if (__ballot(m_blk > mL + kRescaleLog2)) {
+        m_blk = fmaxf(m_blk, shfl_xor_f(m_blk, 16));
+        m_blk = fmaxf(m_blk, shfl_xor_f(m_blk, 32));
+        if (m_blk > mL + kRescaleLog2) {
+          const float f = fast_exp2(mL - m_blk);
+          zL[0] *= f;
+          zL[1] *= f;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          uL[0][dt] *= f0;
-          uL[1][dt] *= f1;
+          for (int dt = 0; dt < C::DT; ++dt) {
+            uL[0][dt] *= f;
+            uL[1][dt] *= f;
+          }
+          mL = m_blk;
         }
-        if (up_in) mL[0] = m_in;
-        if (up_out) mL[1] = m_out;
       }
-      bf16x8 pin, pout;
+      // bf16 weights in pairs, split by the T bits with 16-bit masks (keys
+      // past the chunk have weight 0).  mL is finite here: the first tile of
+      // a chunk holds a valid key for every sample (its first key), and the
+      // exchange above gives every lane of the sample that key's max.
+      uint32_t win[4], wout[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(x[i], c2, -(inT[i] ? mL[0] : mL[1])));
-        const __bf16 pb = (__bf16)p;
-        pin[i] = inT[i] ? pb : (__bf16)0.0f;
-        pout[i] = outT[i] ? pb : (__bf16)0.0f;
+      for (int k = 0; k < 4; ++k) {
+        const float pa = fast_exp2(__builtin_fmaf(x[2 * k], c2, -mL));
+        const float pb = fast_exp2(__builtin_fmaf(x[2 * k + 1], c2, -mL));
+        const uint32_t pk = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)pa, (__bf16)pb});
+        const uint32_t m = pair_mask(in_bits, 2 * k);
+        win[k] = pk & m;
+        wout[k] = pk & ~m;
       }
+      const bf16x8 pin = __builtin_bit_cast(bf16x8, make_uint4(win[0], win[1], win[2], win[3]));
+      const bf16x8 pout = __builtin_bit_cast(bf16x8, make_uint4(wout[0], wout[1], wout[2], wout[3]));
       // ---- U^T += V^T P^T for the two live classes; Z from an all-ones operand
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
@@ -370,9 +381,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (grp == 0) {
-      rS[c * C::REC] = mL[c];
+      rS[c * C::REC] = mL;
       rS[c * C::REC + 1] = zL[c][0];
-      rP[c * C::REC] = mP[c];
+      rP[c * C::REC] = mP;
       rP[c * C::REC + 1] = zP[c][0];
     }
 #pragma unroll
