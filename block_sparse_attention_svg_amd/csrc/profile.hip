@@ -110,7 +110,12 @@ __device__ __forceinline__ void swap_lane(f32x4& a, f32x4& b) {
   b = f32x4{y[0], y[1], y[2], y[3]};
 }
 
-template <int D>
+// ADM8: every frame holds a multiple of 8 tokens and 7 F <= 3 * block, so
+// the 8 keys of a lane (8-aligned) lie in one frame (or all in the text), and
+// their token-major blocks span at most 4 consecutive blocks: the keys'
+// admission then comes from one 64-bit window of the sample's temporal row
+// and four key masks per lane group (admT), instead of one lookup per key.
+template <int D, bool ADM8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void profile_partial_kernel(ProfileArgs a, Geo g) {
   using C = PCfg<D>;
   __shared__ uint4 lds[C::STAGES * C::STRIDE + 64];   // ring stages, then a 1-KB sink
@@ -119,6 +124,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ uint32_t rowS[kQ][kMaxWords + 1];
   __shared__ uint32_t rowT[kQ][kMaxWords + 1];
   __shared__ int blkT[C::STAGES][kTK];
+  // ADM8: per stage and lane group g (keys 8 g .. 8 g + 7 of the tile): the
+  // first key's token-major block bt0, and byte d of the mask word = the keys
+  // whose block is bt0 + d
+  __shared__ uint2 admT[C::STAGES][4];
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -208,7 +217,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
     if (rows < kTK) issue(std::true_type{});   // the chunk's last tile, past N
     else issue(std::false_type{});
-    if (tid < kTK) {
+    if constexpr (ADM8) {
+      if (tid < 4) {
+        const int j0 = min(key0 + 8 * tid, k_end - 1);   // keys past the chunk: any admission
+        int tm0 = j0, step = 1;
+        if (j0 < g.Nv) {
+          const int f = int(g.divS.div(uint32_t(j0)));
+          tm0 = (j0 - f * g.S) * g.F + f;
+          step = g.F;
+        }
+        const int t0 = tm0 & ((1 << g.blk_log2) - 1);
+        uint32_t masks = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int d = (t0 + i * step) >> g.blk_log2;
+          if (d < 4) masks |= 1u << (8 * d + i);
+        }
+        admT[b][tid] = make_uint2(uint32_t(tm0 >> g.blk_log2), masks);
+      }
+    } else if (tid < kTK) {
       const int key = min(key0 + tid, k_end - 1);
       blkT[b][tid] = token_major(key, g) >> g.blk_log2;
     }
@@ -248,10 +275,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto admission = [&](int key0, int b) -> uint32_t {
     const int kblock = min(key0 >> g.blk_log2, a.nB - 1);   // one key block for all 32 keys
     uint32_t bits = (svalid && ((rowS[sidx][kblock >> 5] >> (kblock & 31)) & 1u)) ? 0x100u : 0u;
+    if constexpr (ADM8) {
+      const uint2 e = admT[b][grp];
+      const uint32_t w = e.x >> 5;   // w + 1 <= kMaxWords: the row's padding word at most
+      // bits bt0 .. bt0 + 3 of the temporal row, spread to bytes 0 .. 3
+      const uint32_t win = __builtin_amdgcn_alignbit(rowT[sidx][w + 1], rowT[sidx][w], e.x & 31) & 0xfu;
+      const uint32_t sel = ((win * 0x00204081u) & 0x01010101u) * 0xffu;
+      const uint32_t x = e.y & sel;
+      bits |= (x | (x >> 8) | (x >> 16) | (x >> 24)) & 0xffu;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int bt = blkT[b][8 * grp + i];
-      bits |= ((rowT[sidx][bt >> 5] >> (bt & 31)) & 1u) << i;
+      for (int i = 0; i < 8; ++i) {
+        const int bt = blkT[b][8 * grp + i];
+        bits |= ((rowT[sidx][bt >> 5] >> (bt & 31)) & 1u) << i;
+      }
     }
     return bits;
   };
@@ -572,11 +609,14 @@ void launch_profile(const ProfileArgs& a, hipStream_t st) {
   double* per_sample = reinterpret_cast<double*>(reinterpret_cast<char*>(a.ws) + rec);
   dim3 grid1(a.n_chunks, a.BH);
   dim3 grid2(a.BH, a.n_samples);
+  const bool adm8 = g.S % 8 == 0 && 7 * g.F <= 3 * (1 << g.blk_log2);
   if (a.D == 128) {
-    hipLaunchKernelGGL(profile_partial_kernel<128>, grid1, dim3(kThreads), 0, st, a, g);
+    if (adm8) hipLaunchKernelGGL((profile_partial_kernel<128, true>), grid1, dim3(kThreads), 0, st, a, g);
+    else hipLaunchKernelGGL((profile_partial_kernel<128, false>), grid1, dim3(kThreads), 0, st, a, g);
     hipLaunchKernelGGL(profile_merge_kernel<128>, grid2, dim3(256), 0, st, a, per_sample);
   } else {
-    hipLaunchKernelGGL(profile_partial_kernel<64>, grid1, dim3(kThreads), 0, st, a, g);
+    if (adm8) hipLaunchKernelGGL((profile_partial_kernel<64, true>), grid1, dim3(kThreads), 0, st, a, g);
+    else hipLaunchKernelGGL((profile_partial_kernel<64, false>), grid1, dim3(kThreads), 0, st, a, g);
     hipLaunchKernelGGL(profile_merge_kernel<64>, grid2, dim3(256), 0, st, a, per_sample);
   }
   hipLaunchKernelGGL(profile_choose_kernel, dim3(ceil_div(a.BH, 64)), dim3(64), 0, st, per_sample,
