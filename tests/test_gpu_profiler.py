@@ -170,3 +170,45 @@ def test_near_tie_heads_choose_as_oracle():
     assert np.array_equal(ref_c, [1, 0, 1, 0])
     assert np.array_equal(choice, ref_c)
     assert np.all(rel < ERR_REL)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random shapes (2-11 frames, 4-19 rows, frames of a multiple of 8
+    tokens two times in three and of an odd size otherwise, text tails, both block sizes and head dims,
+    temporal bands of 1-3 blocks, several key chunks).  Each error within
+    PROFILE_ERR_REL of the oracle's, relative to the oracle's value or, for a
+    mask that is nearly exact for the head, to 1e-6 of the head's larger
+    error; the oracle's choice wherever its two errors are more than 3 %
+    apart (closer ties are the near-tie test's); both errors 0 (masks that
+    keep every block) give 0 on the GPU and the spatial mask."""
+    rng = np.random.default_rng(5200 + seed)
+    block = (64, 128)[seed % 2]
+    D = (64, 128)[(seed // 2) % 2]
+    F, Hs = int(rng.integers(2, 12)), int(rng.integers(4, 20))
+    if seed % 3:
+        Ws = 8 * int(rng.integers(1, 5))                  # frames of a multiple of 8 tokens
+    else:
+        Hs, Ws = Hs | 1, 2 * int(rng.integers(1, 15)) + 1   # odd frame sizes
+    text = int(rng.integers(1, 150)) if rng.random() < 0.5 else 0
+    w = S.get_workload("cogvideox", H=2, D=D, F=F, Hs=Hs, Ws=Ws, text=text, block=block,
+                       band_w=int(rng.integers(1, 4)), sigma=float(rng.uniform(0.1, 0.4)), n_spatial=1,
+                       seed=5300 + seed)
+    banner("profile random shape", seed, f"D{D} block {block} {F}x{Hs}x{Ws} + {text} text")
+    q, k, v, cls = S.gen_qkv(w, dtype="bf16")
+    idx = S.sample_query_idx(w, seed)
+    choice, err = _gpu_profile(w, q, k, v, idx)
+    cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+    ref_c, ref_e = O.profile_heads(q[0].float().numpy(), k[0].float().numpy(), v[0].float().numpy(),
+                                   w.F, w.Hs, w.Ws, w.block, w.scale, idx, cand)
+    top = ref_e.max(axis=1, keepdims=True)
+    zero = top[:, 0] == 0
+    assert np.all(err[zero] == 0) and np.all(choice[zero] == 0), (err, choice)
+    den = np.maximum(ref_e, 1e-6 * top)[~zero]
+    rel = np.abs(err[~zero] - ref_e[~zero]) / den
+    print(f"[profile random {seed}] oracle ratios {ref_e[:, 0] / np.maximum(ref_e[:, 1], 1e-300)}, "
+          f"worst relative error deviation {rel.max() if rel.size else 0.0:.2e}")
+    assert np.all(rel < ERR_REL), (rel.max(), err, ref_e)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        clear = np.abs(np.log(ref_e[:, 0] / ref_e[:, 1])) > 0.03
+    assert np.array_equal(choice[clear], ref_c[clear]), (choice, ref_c, ref_e)
