@@ -433,7 +433,6 @@ __global__ __launch_bounds__(512) void row_pattern_kernel(const __bf16* __restri
 // The fp32 pattern values convert exactly to float64, so every product is
 // exact and only the float64 accumulation rounds.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-constexpr int kMaxHs = 64;
 constexpr int kGramWaves = 4;
 
 // Key chunks per frame: enough workgroups for the 256 compute units, chunks a
@@ -472,6 +471,8 @@ __global__ __launch_bounds__(256) void row_gram_part_kernel(const float* __restr
 #if defined(__HIP_DEVICE_COMPILE__)
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, Hs * N * 4, 0x00020000);
+#else
+  (void)base;
 #endif
   uint32_t row_off[RT];
 #pragma unroll
