@@ -187,7 +187,8 @@ def _pattern_bound(q, k, scale, Ws, rows):
 
 
 @pytest.mark.parametrize("F,Hs,Ws,text,D", [(3, 6, 20, 10, 64), (2, 4, 100, 0, 128), (4, 16, 16, 0, 64),
-                                            (3, 5, 33, 7, 128), (1, 3, 128, 50, 64)])
+                                            (3, 5, 33, 7, 128), (1, 3, 128, 50, 64), (2, 20, 4, 3, 64),
+                                            (2, 37, 3, 0, 128), (2, 50, 3, 5, 128), (1, 64, 2, 9, 64)])
 def test_row_similarity_matches_oracle(F, Hs, Ws, text, D):
     banner(f"row similarity F={F} Hs={Hs} Ws={Ws} D={D}")
     N = F * Hs * Ws + text
