@@ -58,7 +58,8 @@ def _qk(B_, H, N, D, seed, spread=1.0):
     return q, k
 
 
-@pytest.mark.parametrize("D,block,N", [(64, 64, 1024), (128, 128, 1000), (64, 128, 777), (128, 64, 600)])
+@pytest.mark.parametrize("D,block,N", [(64, 64, 1024), (128, 128, 1000), (64, 128, 777), (128, 64, 600),
+                                         (128, 128, 128), (64, 128, 130), (128, 128, 1)])
 def test_block_energy_matches_oracle(D, block, N):
     banner(f"energy D={D} block={block} N={N}")
     q, k = _qk(1, 2, N, D, seed=D + block + N, spread=1.3)
