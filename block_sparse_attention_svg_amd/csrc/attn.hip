@@ -1231,7 +1231,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint32_t* __restrict__ 
 // Work list of each XCD: the ranges plan_kernel gave it, head after head,
 // stably partitioned so that heavy pairs (more than half of all key blocks in
 // the union of their two rows, e.g. the dense rows of text queries) come
-// first and start early.  One workgroup per XCD.
+// first and start early.  One workgroup per XCD.  Each head's range and list
+// entry fields are read once into LDS (up to kOrderLdsHeads heads; beyond
+// that they are read from global memory at each use).
+constexpr int kOrderLdsHeads = 2048;
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ head_mask,
                                                     const int32_t* __restrict__ head_layout, int n_masks,
                                                     int n_kb, int BH, int pairs, int cap,
@@ -1241,33 +1244,50 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
   int32_t* counts = plan + BH * 9;
   int2* list = reinterpret_cast<int2*>(plan + attn_plan_list_offset(BH)) + int64_t(x) * cap;
   __shared__ long long tmp[256];
-  // items of this XCD, head-major: item g of head h is pair split[h][x] + g - base(h)
+  __shared__ int4 head_s[kOrderLdsHeads];
+  const bool in_lds = BH <= kOrderLdsHeads;
+  // head h: first pair and length of its range on this XCD, and the list
+  // entry's fields: x = h | token-major << 31, y = mask << 16 (pair added)
+  auto head_info = [&](int h) -> int4 {
+    int m = head_mask ? head_mask[h] : h % n_masks;
+    m = min(max(m, 0), n_masks - 1);
+    const bool tm = head_layout && head_layout[h] != 0;
+    return make_int4(split[h * 9 + x], split[h * 9 + x + 1] - split[h * 9 + x],
+                     h | (tm ? int(0x80000000u) : 0), m << 16);
+  };
+  auto info = [&](int h) -> int4 { return in_lds ? head_s[h] : head_info(h); };
+  // items of this XCD, head-major: item g of head h is pair start(h) + g - base(h)
   long long len_sum = 0;
-  for (int h = tid; h < BH; h += 256) len_sum += split[h * 9 + x + 1] - split[h * 9 + x];
+  for (int h = tid; h < BH; h += 256) {
+    const int4 hi = head_info(h);
+    if (in_lds) head_s[h] = hi;
+    len_sum += hi.y;
+  }
   long long total_ll = 0;
-  block_scan256(len_sum, tmp, total_ll);
+  block_scan256(len_sum, tmp, total_ll);   // its barriers also publish head_s
   const int total = int(total_ll);
   const int chunk = (total + 255) / 256;
   const int g0 = min(tid * chunk, total), g1 = min(g0 + chunk, total);
   auto walk = [&](auto f) {
     int h = 0, base = 0;
-    while (h < BH && base + (split[h * 9 + x + 1] - split[h * 9 + x]) <= g0) {
-      base += split[h * 9 + x + 1] - split[h * 9 + x];
-      ++h;
+    int4 hi = BH > 0 ? info(0) : make_int4(0, 0, 0, 0);
+    while (h < BH && base + hi.y <= g0) {
+      base += hi.y;
+      if (++h < BH) hi = info(h);
     }
     for (int g = g0; g < g1; ++g) {
-      while (g - base >= split[h * 9 + x + 1] - split[h * 9 + x]) {
-        base += split[h * 9 + x + 1] - split[h * 9 + x];
-        ++h;
+      while (g - base >= hi.y) {
+        base += hi.y;
+        hi = info(++h);
       }
-      f(h, split[h * 9 + x] + (g - base));
+      f(hi, h, hi.x + (g - base));
     }
   };
   const int32_t* work = plan + attn_plan_work_offset(BH, pairs);
   auto heavy = [&](int h, int p) -> bool { return 2 * (work[int64_t(h) * pairs + p] - 2) > n_kb; };
   uint64_t flags = 0;   // heavy flags of this thread's items (chunk <= 64), else recomputed
   int mine = 0, i = 0;
-  walk([&](int h, int p) {
+  walk([&](const int4&, int h, int p) {
     const bool hv = heavy(h, p);
     if (i < 64 && hv) flags |= uint64_t(1) << i;
     mine += hv;
@@ -1280,16 +1300,11 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
   i = 0;
   // item (h, p) as x = h | token-major << 31, y = p | mask << 16, so that the
   // attention kernel needs no further load to address its operands
-  auto entry = [&](int h, int p) {
-    int m = head_mask ? head_mask[h] : h % n_masks;
-    m = min(max(m, 0), n_masks - 1);
-    const bool tm = head_layout && head_layout[h] != 0;
-    return make_int2(h | (tm ? int(0x80000000u) : 0), p | (m << 16));
-  };
-  walk([&](int h, int p) {
+  walk([&](const int4& hi, int h, int p) {
     const bool hv = i < 64 ? ((flags >> i) & 1) != 0 : heavy(h, p);
-    if (hv) list[hp++] = entry(h, p);
-    else list[np++] = entry(h, p);
+    const int2 e = make_int2(hi.z, p | hi.w);
+    if (hv) list[hp++] = e;
+    else list[np++] = e;
     ++i;
   });
   if (tid == 0) {

@@ -456,6 +456,7 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, doubl
   __shared__ float M[4];
   __shared__ float Z[4];
   __shared__ float Wc[4][kMergeCache];
+  __shared__ float Us[4][D];
   __shared__ double red[2][4];
   const float* base = a.ws + (int64_t(bh) * a.n_chunks * kQ + sidx) * 4 * C::REC;
   const int64_t chunk_stride = int64_t(kQ) * 4 * C::REC;
@@ -482,11 +483,11 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, doubl
     }
   }
   __syncthreads();
-  double e[2] = {0.0, 0.0};
-  for (int d = tid; d < D; d += 256) {
-    float U[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+  // U of class c = wave, channels lane, lane + 64, ...: the chunk chain of one
+  // (class, channel) per thread and step, the four classes side by side
+  {
+    const int c = wave;
+    for (int d = lane; d < D; d += 64) {
       float u0 = 0.f, u1 = 0.f;
       const float* r = base + c * C::REC + 4 + d;
       int ch = 0;
@@ -497,8 +498,15 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, doubl
         u1 += r[(ch + 1) * chunk_stride] * w1;
       }
       if (ch < nc) u0 += r[ch * chunk_stride] * (ch < kMergeCache ? Wc[c][ch] : weight(c, ch, M[c]));
-      U[c] = u0 + u1;
+      Us[c][d] = u0 + u1;
     }
+  }
+  __syncthreads();
+  double e[2] = {0.0, 0.0};
+  for (int d = tid; d < D; d += 256) {
+    float U[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) U[c] = Us[c][d];
 #pragma unroll
     for (int mask = 0; mask < 2; ++mask) {
       // spatial keeps classes {0, 1}; temporal keeps {0, 2}
@@ -545,15 +553,23 @@ __global__ __launch_bounds__(256) void profile_merge_kernel(ProfileArgs a, doubl
   }
 }
 
-__global__ void profile_choose_kernel(const double* __restrict__ per_sample, int BH, int n_samples,
-                                      int32_t* __restrict__ choice, float* __restrict__ err) {
-  const int bh = blockIdx.x * blockDim.x + threadIdx.x;
-  if (bh >= BH) return;
+// One wave per head: lane s loads sample s's two errors, a butterfly sums
+// them (a fixed order, so repeated calls agree bit for bit).
+__global__ __launch_bounds__(64) void profile_choose_kernel(const double* __restrict__ per_sample, int BH,
+                                                            int n_samples, int32_t* __restrict__ choice,
+                                                            float* __restrict__ err) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
   double es = 0.0, et = 0.0;
-  for (int s = 0; s < n_samples; ++s) {
-    es += per_sample[(int64_t(bh) * kQ + s) * 2 + 0];
-    et += per_sample[(int64_t(bh) * kQ + s) * 2 + 1];
+  if (lane < n_samples) {
+    es = per_sample[(int64_t(bh) * kQ + lane) * 2 + 0];
+    et = per_sample[(int64_t(bh) * kQ + lane) * 2 + 1];
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    es += __shfl_xor(es, off, 64);
+    et += __shfl_xor(et, off, 64);
+  }
+  if (lane != 0) return;
   choice[bh] = es <= et ? 0 : 1;
   if (err) {
     err[2 * bh + 0] = float(es);
@@ -571,13 +587,15 @@ size_t profile_workspace_bytes(int BH, int N, int D, int block, int n_samples, i
                                int* n_chunks) {
   (void)block;
   (void)n_samples;
-  // Chunking: the partial kernel runs two workgroups per CU, 512 at a time on
-  // the 256 CUs of an MI355X.  The chunk length (whole 32-key tiles, at most
-  // kChunkKeys keys) minimises a cost in units of one tile's time: rounds of
-  // workgroups x (tiles per workgroup + about 3 tiles of set-up), plus the
-  // chunk records written and merged (about 0.031 tile per record set of a
-  // head, 64 samples x 4 classes x (D + 4) floats, at HBM speed).
-  constexpr int kSlots = 512;
+  // Chunking: the partial kernel runs two workgroups per CU at D = 128 (its
+  // registers) and three at D = 64 (143 registers, 52 KB of LDS each): 512 or
+  // 768 at a time on the 256 CUs of an MI355X.  The chunk length (whole 32-key
+  // tiles, at most kChunkKeys keys) minimises a cost in units of one tile's
+  // time: rounds of workgroups x (tiles per workgroup + about 3 tiles of
+  // set-up), plus the chunk records written and merged (about 0.031 tile per
+  // record set of a head, 64 samples x 4 classes x (D + 4) floats, at HBM
+  // speed).
+  const int kSlots = D == 64 ? 768 : 512;
   int ck = kTK, nc = ceil_div(N, kTK);
   long best = -1;
   for (int t = kTK; t <= kChunkKeys; t += kTK) {
@@ -619,7 +637,7 @@ void launch_profile(const ProfileArgs& a, hipStream_t st) {
     else hipLaunchKernelGGL((profile_partial_kernel<64, false>), grid1, dim3(kThreads), 0, st, a, g);
     hipLaunchKernelGGL(profile_merge_kernel<64>, grid2, dim3(256), 0, st, a, per_sample);
   }
-  hipLaunchKernelGGL(profile_choose_kernel, dim3(ceil_div(a.BH, 64)), dim3(64), 0, st, per_sample,
+  hipLaunchKernelGGL(profile_choose_kernel, dim3(a.BH), dim3(64), 0, st, per_sample,
                      a.BH, a.n_samples, a.choice, a.err);
 }
 
