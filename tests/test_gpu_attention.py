@@ -297,6 +297,59 @@ def test_many_small_heads_through_the_work_queues():
         assert np.max(np.abs(lse1[0, h].cpu().numpy() - ref_lse)) < LSE_ABS
 
 
+def test_more_heads_than_the_order_kernels_lds_table():
+    """B x H = 2 x 1100 heads (more than the 2048 head ranges the work-list
+    kernel keeps in LDS, so it reads them from global memory) of 300 tokens
+    in mixed layouts through the fused path: the same bits as the two batch
+    rows run as separate calls (1100 heads each, ranges in LDS), and sampled
+    heads against the oracle."""
+    banner("attn heads past the LDS table")
+    B, H, F, Hs, Ws, D = 2, 1100, 3, 10, 10, 64
+    N = F * Hs * Ws
+    g = torch.Generator().manual_seed(95)
+    q, k, v = (torch.randn(B, H, N, D, generator=g).to(torch.bfloat16) for _ in range(3))
+    s = svg.Shape(B, H, N, D, F, Hs, Ws, 128)
+    s1 = svg.Shape(1, H, N, D, F, Hs, Ws, 128)
+    nB = s.n_blocks
+    rng = np.random.default_rng(96)
+    M = (rng.random((5, nB, nB)) < 0.6).astype(np.uint8)
+    M[:, :, 0] = 1
+    enc = svg.svg_encode_mask(torch.from_numpy(M).to(DEV))
+    hm_np = rng.integers(0, 5, B * H).astype(np.int32)
+    lay_np = rng.integers(0, 2, B * H).astype(np.int32)
+    hm, lay = torch.from_numpy(hm_np).to(DEV), torch.from_numpy(lay_np).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    kp = svg.svg_permute(kd, s, lay)
+    o, _, lse = svg.svg_block_sparse_attn(qd, kd, vd, s, 0.125, enc, head_mask=hm, head_layout=lay,
+                                          kp=kp, lse=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        sl = slice(b * H, (b + 1) * H)
+        ob, _, lseb = svg.svg_block_sparse_attn(qd[b:b + 1], kd[b:b + 1], vd[b:b + 1], s1, 0.125, enc,
+                                                head_mask=hm[sl].contiguous(),
+                                                head_layout=lay[sl].contiguous(),
+                                                kp=kp[b:b + 1].contiguous(), lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[b], ob[0]), f"batch row {b}"
+        assert torch.equal(lse[b], lseb[0]), f"batch row {b} lse"
+    perm = O.token_major_index(F, Hs, Ws, N)
+    sample = []   # per batch row and layout, the first and the last such head
+    for b in range(B):
+        for layout in (0, 1):
+            hs = np.flatnonzero(lay_np[b * H:(b + 1) * H] == layout)
+            sample += [(b, int(hs[0])), (b, int(hs[-1]))]
+    for b, h in sample:
+        i = b * H + h
+        ref, ref_lse = O.head_attention(q[b, h].float().numpy(), k[b, h].float().numpy(),
+                                        v[b, h].float().numpy(), M[hm_np[i]], int(lay_np[i]), F, Hs, Ws,
+                                        128, 0.125)
+        assert_attn_close(to_np(o[b, h]), ref, f"head ({b}, {h}) layout {lay_np[i]}")
+        got_lse = lse[b, h].cpu().numpy()          # in the layout the head attends in
+        if lay_np[i]:
+            got_lse = got_lse[perm]
+        assert np.max(np.abs(got_lse - ref_lse)) < LSE_ABS
+
+
 def test_fused_layout_batch2_mixed_layouts():
     """B = 2 with a text tail and per-(batch, head) layouts: the fused layout
     gives the bits of the separate permutation moves."""
