@@ -361,10 +361,16 @@ __device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict_
 }
 
 // O^T (D x 32 queries) += V^T P^T, the V^T operands of key step s+1 in flight
-// while step s computes.
-template <int D>
+// while step s computes.  With MS (matrix-core sum) every step also adds its
+// 16 keys' weights into the denominator on the matrix core: one
+// v_mfma_f32_16x16x32_bf16 with the weights as the B operand and the 0/1
+// selector `sel` as A (lane l: rows 4i of A take the contraction groups
+// l/16 = 0, 2, which hold queries 0-15, rows 4i+1 the groups 1, 3, queries
+// 16-31), so accumulator register 0 of lane l sums query l%16 and register 1
+// query 16 + l%16 over every key of the block.
+template <int D, bool MS = false>
 __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf16x8* pb,
-                                        f32x16* oacc) {
+                                        f32x16* oacc, const bf16x8& sel, f32x4& lacc) {
   using C = Cfg2<D>;
   constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
   uint4 cur[C::DT], nxt[C::DT];
@@ -382,6 +388,7 @@ __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
       oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur[dt]), pb[s], oacc[dt], 0, 0, 0);
+    if constexpr (MS) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[s], lacc, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) cur[dt] = nxt[dt];
@@ -390,10 +397,13 @@ __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf
 
 // Online softmax of one 128-key block: S (raw logits) -> P (bf16), updating the
 // running max m (log2 units, moved only when the block max exceeds it by more
-// than 2^8), the lane's share of the denominator and, on a move, O.
-template <int D>
+// than 2^8), the lane's share of the denominator and, on a move, O.  With MS
+// the denominator is summed from the bf16 weights on the matrix core
+// (mfma_pv) and only rescaled here.
+template <int D, bool MS = false>
 __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* oacc, float& m_run,
-                                              float& l_part, int key0, int N, int h, float c2) {
+                                              float& l_part, f32x4& lacc, int key0, int N, int h,
+                                              float c2) {
   using C = Cfg2<D>;
   if (key0 + C::BLK > N) {
 #pragma unroll
@@ -412,10 +422,19 @@ __device__ __forceinline__ void softmax_block(f32x16* sacc, bf16x8* pb, f32x16* 
   mx = max_cross_half(mx) * c2;
   if (mx > m_run + kRescaleLog2) {
     const float alpha = fast_exp2(m_run - mx);
-    l_part *= alpha;
+    if constexpr (MS) lacc *= alpha;
+    else l_part *= alpha;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
     m_run = mx;
+  }
+  if constexpr (MS) {
+#pragma unroll
+    for (int s = 0; s < C::PS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pb[s][i] = (__bf16)fast_exp2(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + i], c2, -m_run));
+    return;
   }
   // The denominator sums the fp32 weights with plain adds (two chains): a
   // bf16 dot2 would have to wait for the matrix core, which the partner wave
@@ -563,7 +582,7 @@ __device__ __forceinline__ void softmax_block8(f32x16* sacc, i32x8* pb, f32x16* 
 // workgroup calls it; it synchronizes.  In its last key-block iteration
 // thread 0 takes the index of its next item from the queue head `qhead` into
 // `next_idx`, so that the atomic's round trip overlaps the item's last blocks.
-template <int D>
+template <int D, bool MS>
 __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, int mask_id, bool tm,
                                           int32_t* qhead, int& next_idx) {
   using C = Cfg2<D>;
@@ -654,6 +673,16 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   float l_part = 0.f;
   f32x16 sacc[C::KT];
   bf16x8 pb[C::PS];
+  // MS: denominator on the matrix core (mfma_pv); selector of lane l is 1 on
+  // rows 4i (contraction groups 0, 2) or 4i + 1 (groups 1, 3)
+  f32x4 lacc = f32x4{};
+  bf16x8 sel;
+  {
+    const __bf16 one = ((lane >> 4) & 1) ? __bf16((lane & 3) == 1 ? 1.f : 0.f)
+                                         : __bf16((lane & 3) == 0 ? 1.f : 0.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sel[i] = one;
+  }
 
   __shared__ SeqLds sl;
   int seq_w = 0, seq_j = 1;
@@ -703,11 +732,11 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
 
     // ---- phase 1 --------------------------------------------------------------
     if (grp == 0) {
-      if (have_prev && mine_prev) mfma_pv<D>(v_prev, v_lane, pb, oacc);
+      if (have_prev && mine_prev) mfma_pv<D, MS>(v_prev, v_lane, pb, oacc, sel, lacc);
       if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
     } else {
       if (have_prev && mine_prev)
-        softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_prev * C::BLK, N, h, c2);
+        softmax_block<D, MS>(sacc, pb, oacc, m_run, l_part, lacc, kb_prev * C::BLK, N, h, c2);
     }
     // No barrier between the phases: the groups share no data within an
     // iteration (each holds its own S, P and O; the copies of this iteration
@@ -723,9 +752,9 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
       copy_v(v_src(kb_cur, have_cur), vb_lds[kbuf]);
       __builtin_amdgcn_sched_barrier(0);
       if (have_cur && mine_cur)
-        softmax_block<D>(sacc, pb, oacc, m_run, l_part, kb_cur * C::BLK, N, h, c2);
+        softmax_block<D, MS>(sacc, pb, oacc, m_run, l_part, lacc, kb_cur * C::BLK, N, h, c2);
     } else {
-      if (have_prev && mine_prev) mfma_pv<D>(v_prev, v_lane, pb, oacc);
+      if (have_prev && mine_prev) mfma_pv<D, MS>(v_prev, v_lane, pb, oacc, sel, lacc);
       if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -747,7 +776,7 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l_tot = l_part + shfl_xor_f(l_part, 32);
+  const float l_tot = MS ? ((lane & 16) ? lacc[1] : lacc[0]) : l_part + shfl_xor_f(l_part, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   {
     // lane indices recomputed here rather than kept live through the loop
@@ -911,6 +940,7 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY;
   float l_part = 0.f;
+  f32x4 l_dummy = f32x4{};   // bf16 helpers' matrix-core sum, unused here
   f32x16 sacc[C::KT];
   using PReg = std::conditional_t<F8, i32x8, bf16x8>;
   PReg pb[F8 ? C::PG : C::PS];
@@ -964,11 +994,11 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
   };
   auto pv = [&](const char* v_lds) {
     if constexpr (F8) mfma_pv8<D>(v_lds, v_lane, pb, oacc);
-    else mfma_pv<D>(v_lds, v_lane, pb, oacc);
+    else mfma_pv<D>(v_lds, v_lane, pb, oacc, pb[0], l_dummy);
   };
   auto smax = [&](int key0) {
     if constexpr (F8) softmax_block8<D>(sacc, pb, oacc, m_run, l_part, key0, N, h, c2);
-    else softmax_block<D>(sacc, pb, oacc, m_run, l_part, key0, N, h, c2);
+    else softmax_block<D>(sacc, pb, oacc, m_run, l_part, l_dummy, key0, N, h, c2);
   };
 
   // Iteration j uses K buffer j%2 and V buffer (j-1)%2; unrolled by two so
@@ -1095,7 +1125,7 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
 // queue head.  A workgroup whose list is done takes items from the other
 // XCDs' lists.  Every item is computed the same way wherever it runs, so the
 // result does not depend on the schedule.
-template <int D, bool F8>
+template <int D, bool F8, bool MS = false>
 __device__ __forceinline__ void persistent_items(const AttnArgs& a, int cap) {
   const int xcd = blockIdx.x % 8;
   const int32_t* counts = a.plan + a.BH * 9;
@@ -1126,7 +1156,7 @@ __device__ __forceinline__ void persistent_items(const AttnArgs& a, int cap) {
     if constexpr (F8)
       attn_pair_f8<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
     else
-      attn_pair<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
+      attn_pair<D, MS>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
     // attn_pair ends with no barrier: the next take must not overwrite
     // `grabbed` before every wave has read it, nor the next item's copies
     // land in tiles a slow wave still reads for its output
@@ -1134,9 +1164,11 @@ __device__ __forceinline__ void persistent_items(const AttnArgs& a, int cap) {
   }
 }
 
-template <int D>
+// MS: the denominator summed on the matrix core from the bf16 weights (taken
+// when no LSE is asked for: the LSE needs the fp32 sum).
+template <int D, bool MS>
 __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap) {
-  persistent_items<D, false>(a, cap);
+  persistent_items<D, false, MS>(a, cap);
 }
 
 // The same schedule with FP8 (E4M3) operands for both products.
@@ -1418,8 +1450,19 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.head_mask, a.head_layout, a.n_masks,
                      a.n_kb, a.BH, pairs, a.BH * per_xcd, a.plan);
   const dim3 grid(persistent_grid(int64_t(a.BH) * pairs));
-  if constexpr (F8) hipLaunchKernelGGL((attn_fwd_fp8_kernel<D>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
-  else hipLaunchKernelGGL((attn_fwd_b128_kernel<D>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  // D = 64 is bound by the softmax's VALU work: its denominator moves to the
+  // matrix core unless the LSE is asked for.  At D = 128 the kernel is at the
+  // register limit and the matrix cores are the busier unit: fp32 adds.
+  if constexpr (F8) {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  } else if constexpr (D == 64) {
+    if (a.lse == nullptr)
+      hipLaunchKernelGGL((attn_fwd_b128_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+    else
+      hipLaunchKernelGGL((attn_fwd_b128_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_b128_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  }
 }
 
 }  // namespace

@@ -4,7 +4,7 @@ and 128 tokens, latent grids from a single token per frame to 23 x 39, one
 to six frames, text tails of up to 200 tokens, random masks of any density
 (with an empty row, a dense row and a dense last column), mixed layouts.
 128-token blocks run the layer's fused flow (svg_prepare_kv, Q and O through
-the permutation inside the call) and, for D = 128 and 64, the FP8 variant
+the permutation inside the call), with and without the LSE, and, for D = 128 and 64, the FP8 variant
 against its derived bound; 64-token blocks run the token-major twins.
 """
 import numpy as np
@@ -64,7 +64,11 @@ def test_random_config_matches_oracle(seed):
         kp, vt = svg.svg_prepare_kv(kd, vd, s, head_layout=layd)
         o, _, lse = svg.svg_block_sparse_attn(qd, kd, None, s, scale, enc, head_mask=hm, head_layout=layd,
                                               kp=kp, vt=vt, lse=True)
-        outs = [o]
+        # without the LSE (at D = 64 the denominator is then summed on the
+        # matrix core from the bf16 weights)
+        o2, _, _ = svg.svg_block_sparse_attn(qd, kd, None, s, scale, enc, head_mask=hm, head_layout=layd,
+                                             kp=kp, vt=vt)
+        outs = [o, o2]
     else:
         qp, kp, vp = (svg.svg_permute(t, s, layd) for t in (qd, kd, vd))
         o, op, lse = svg.svg_block_sparse_attn(qd, kd, vd, s, scale, enc, head_mask=hm, head_layout=layd,
@@ -81,6 +85,11 @@ def test_random_config_matches_oracle(seed):
             else:
                 got = to_np(outs[1][b, h])[p]
             assert_attn_close(got, ref, f"seed {seed} head {bh}")
+            if s.block == 128:
+                got2 = to_np(outs[1][b, h])
+                assert_attn_close(got2, ref, f"seed {seed} head {bh} (no LSE)")
+                if s.D == 128:
+                    assert np.array_equal(got2, got), f"seed {seed} head {bh}: output depends on the LSE request"
             g = lse[b, h].cpu().numpy()
             fin = np.isfinite(ref_lse)
             assert np.array_equal(np.isneginf(g), ~fin), f"seed {seed} head {bh}: empty rows"
