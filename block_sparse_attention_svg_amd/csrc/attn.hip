@@ -503,9 +503,13 @@ __device__ __forceinline__ void mfma_qk8(const char* kb_lds, int k_lane, const i
 }
 
 // O^T (D x 32 queries) += V^T P^T over the two 64-key groups of a block.
-template <int D>
+// With MS the group's weights are also summed into the denominator on the
+// matrix core, as in mfma_pv: one v_mfma_f32_16x16x128_f8f6f4 per 64-key
+// group with the E4M3 weights as B and the 0/1 selector `sel` as A (bytes of
+// lane l cover row l%16 and contraction 32*(l/16) + i in that form).
+template <int D, bool MS = false>
 __device__ __forceinline__ void mfma_pv8(const char* vb_lds, int v_lane, const i32x8* pb,
-                                         f32x16* oacc) {
+                                         f32x16* oacc, const i32x8& sel, f32x4& lacc) {
   using C = Cfg2<D, true>;
   constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
   i32x8 cur[C::DT], nxt[C::DT];
@@ -521,6 +525,7 @@ __device__ __forceinline__ void mfma_pv8(const char* vb_lds, int v_lane, const i
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = mfma_f8(cur[dt], pb[g], oacc[dt]);
+    if constexpr (MS) lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[g], lacc, 0, 0, 0, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) cur[dt] = nxt[dt];
@@ -529,10 +534,12 @@ __device__ __forceinline__ void mfma_pv8(const char* vb_lds, int v_lane, const i
 
 // Online softmax of one 128-key block for the FP8 products: as softmax_block,
 // with the weights rounded to E4M3 (nearest even) for the PV product and
-// packed in contraction order.
-template <int D>
+// packed in contraction order.  With MS the denominator is summed from the
+// E4M3 weights on the matrix core (mfma_pv8) and only rescaled here.
+template <int D, bool MS = false>
 __device__ __forceinline__ void softmax_block8(f32x16* sacc, i32x8* pb, f32x16* oacc, float& m_run,
-                                               float& l_part, int key0, int N, int h, float c2) {
+                                               float& l_part, f32x4& lacc, int key0, int N, int h,
+                                               float c2) {
   using C = Cfg2<D, true>;
   if (key0 + C::BLK > N) {
 #pragma unroll
@@ -551,7 +558,8 @@ __device__ __forceinline__ void softmax_block8(f32x16* sacc, i32x8* pb, f32x16* 
   mx = max_cross_half(mx) * c2;
   if (mx > m_run + kRescaleLog2) {
     const float alpha = fast_exp2(m_run - mx);
-    l_part *= alpha;
+    if constexpr (MS) lacc *= alpha;
+    else l_part *= alpha;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
     m_run = mx;
@@ -566,15 +574,17 @@ __device__ __forceinline__ void softmax_block8(f32x16* sacc, i32x8* pb, f32x16* 
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         p[b] = fast_exp2(__builtin_fmaf(sacc[kt][r0 + b], c2, -m_run));
-        if (b & 1) l1 += p[b];
-        else l0 += p[b];
+        if constexpr (!MS) {
+          if (b & 1) l1 += p[b];
+          else l0 += p[b];
+        }
       }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
       pb[g][w] = word;
     }
   }
-  l_part += l0 + l1;
+  if constexpr (!MS) l_part += l0 + l1;
 }
 
 // One work item: query blocks 2*pair and 2*pair+1 of head bh, which uses
@@ -832,7 +842,7 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
 // workgroup calls it; it synchronizes.  In its last key-block iteration
 // thread 0 takes the index of its next item from the queue head `qhead` into
 // `next_idx`, so that the atomic's round trip overlaps the item's last blocks.
-template <int D>
+template <int D, bool MS>
 __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair, int mask_id, bool tm,
                                              int32_t* qhead, int& next_idx) {
   constexpr bool F8 = true;
@@ -940,7 +950,15 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY;
   float l_part = 0.f;
-  f32x4 l_dummy = f32x4{};   // bf16 helpers' matrix-core sum, unused here
+  // MS: denominator on the matrix core (mfma_pv8); selector bytes of lane l
+  // are E4M3 1.0 on rows 4i (contraction groups 0, 2) or 4i + 1 (groups 1, 3)
+  f32x4 lacc = f32x4{};
+  i32x8 sel8;
+  {
+    const int one = ((lane >> 4) & 1) ? ((lane & 3) == 1 ? 0x38383838 : 0) : ((lane & 3) == 0 ? 0x38383838 : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sel8[i] = one;
+  }
   f32x16 sacc[C::KT];
   using PReg = std::conditional_t<F8, i32x8, bf16x8>;
   PReg pb[F8 ? C::PG : C::PS];
@@ -993,12 +1011,12 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
     else mfma_qk<D>(k_lds, k_lane, qreg, sacc);
   };
   auto pv = [&](const char* v_lds) {
-    if constexpr (F8) mfma_pv8<D>(v_lds, v_lane, pb, oacc);
-    else mfma_pv<D>(v_lds, v_lane, pb, oacc, pb[0], l_dummy);
+    if constexpr (F8) mfma_pv8<D, MS>(v_lds, v_lane, pb, oacc, sel8, lacc);
+    else mfma_pv<D>(v_lds, v_lane, pb, oacc, pb[0], lacc);
   };
   auto smax = [&](int key0) {
-    if constexpr (F8) softmax_block8<D>(sacc, pb, oacc, m_run, l_part, key0, N, h, c2);
-    else softmax_block<D>(sacc, pb, oacc, m_run, l_part, l_dummy, key0, N, h, c2);
+    if constexpr (F8) softmax_block8<D, MS>(sacc, pb, oacc, m_run, l_part, lacc, key0, N, h, c2);
+    else softmax_block<D>(sacc, pb, oacc, m_run, l_part, lacc, key0, N, h, c2);
   };
 
   // Iteration j uses K buffer j%2 and V buffer (j-1)%2; unrolled by two so
@@ -1063,7 +1081,7 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l_tot = l_part + shfl_xor_f(l_part, 32);
+  const float l_tot = MS ? ((lane & 16) ? lacc[1] : lacc[0]) : l_part + shfl_xor_f(l_part, 32);
   const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
   {
     // lane indices recomputed here rather than kept live through the loop
@@ -1154,7 +1172,7 @@ __device__ __forceinline__ void persistent_items(const AttnArgs& a, int cap) {
     const int iy = __builtin_amdgcn_readfirstlane(grabbed.y);
     if (iy < 0) break;
     if constexpr (F8)
-      attn_pair_f8<D>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
+      attn_pair_f8<D, MS>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
     else
       attn_pair<D, MS>(a, ix & 0x7fffffff, iy & 0xffff, int(uint32_t(iy) >> 16), ix < 0, heads + xcd, next_idx);
     // attn_pair ends with no barrier: the next take must not overwrite
@@ -1171,10 +1189,11 @@ __global__ __launch_bounds__(512) void attn_fwd_b128_kernel(AttnArgs a, int cap)
   persistent_items<D, false, MS>(a, cap);
 }
 
-// The same schedule with FP8 (E4M3) operands for both products.
-template <int D>
+// The same schedule with FP8 (E4M3) operands for both products.  MS as in
+// attn_fwd_b128_kernel.
+template <int D, bool MS>
 __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(AttnArgs a, int cap) {
-  persistent_items<D, true>(a, cap);
+  persistent_items<D, true, MS>(a, cap);
 }
 
 // Work of query-block pair p of a mask: key blocks in the union of its two
@@ -1451,10 +1470,17 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
                      a.n_kb, a.BH, pairs, a.BH * per_xcd, a.plan);
   const dim3 grid(persistent_grid(int64_t(a.BH) * pairs));
   // D = 64 is bound by the softmax's VALU work: its denominator moves to the
-  // matrix core unless the LSE is asked for.  At D = 128 the kernel is at the
-  // register limit and the matrix cores are the busier unit: fp32 adds.
-  if constexpr (F8) {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  // matrix core unless the LSE is asked for (bf16 and FP8).  At D = 128 the
+  // kernels are at the register limit (the FP8 one then spills in its loop,
+  // 18 % slower at Wan) and the bf16 one is held by the board's power limit
+  // (no gain): fp32 adds.
+  if constexpr (F8 && D == 64) {
+    if (a.lse == nullptr)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+    else
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
+  } else if constexpr (F8) {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
   } else if constexpr (D == 64) {
     if (a.lse == nullptr)
       hipLaunchKernelGGL((attn_fwd_b128_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);

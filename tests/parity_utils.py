@@ -76,10 +76,20 @@ def sample_qblocks(n_blocks: int, seed: int, n: int = 32, must=()):
 FP8_MMA_REL = 2.0 ** -11
 
 
-def fp8_bound(qd, kd, vd, M, B, scale, qblocks):
+def fp8_bound(qd, kd, vd, M, B, scale, qblocks, self_norm=False):
     """Per-element bound on |o_fp8 - o| and per-row bound on |lse_fp8 - lse| of
     one head (float64 [N, D] and [N]; NaN outside qblocks), o and lse being
-    the oracle's attention on the dequantized q, k, v in the mask's layout."""
+    the oracle's attention on the dequantized q, k, v in the mask's layout.
+
+    self_norm: the output's denominator is the matrix core's sum of the E4M3
+    weights themselves (the D = 64 call without LSE) instead of the fp32
+    weights: o' = sum q_j v_j / sum q_j with q_j = w_j + d_j, so
+    o' - o_w = sum d_j (v_j - o_w) / sum q_j, at most
+    (sum |d_j| |v_j| + |o_w| sum |d_j|) / (z - sum |d_j|) (every |d_j| <= w_j
+    and the row's largest weight is >= 1, so the denominator stays positive),
+    each weight first moved by the score error (|d_j| <= 2^-4 w_j e^E), plus
+    the matrix core's accumulation of the sum and of the product (2^-11 of
+    sum q_j and of sum q_j |v_j| each, taken as 2^-10 of both terms)."""
     N, D = qd.shape
     bnd = np.full((N, D), np.nan)
     e_lse = np.full(N, np.nan)
@@ -102,7 +112,14 @@ def fp8_bound(qd, kd, vd, M, B, scale, qblocks):
         E = (FP8_MMA_REL * scale * (q_abs[rows] @ k_abs[keys].T).max(axis=1, keepdims=True)
              + 2.0 ** -20 * np.abs(s).max(axis=1, keepdims=True))
         dw = np.where(w >= 2.0 ** -6, 2.0 ** -4 * w, np.maximum(2.0 ** -4 * w, np.minimum(w, 2.0 ** -10)))
-        t_p = (dw @ np.abs(v)) / z
+        if self_norm:
+            dw = dw * np.exp(E)
+            zq = z - dw.sum(axis=1, keepdims=True)
+            oo_w = (w @ np.abs(v)) / z
+            t_p = (dw @ np.abs(v) + np.abs(oo) * dw.sum(axis=1, keepdims=True)) / zq \
+                + 2.0 ** -10 * (oo_w + np.abs(oo))
+        else:
+            t_p = (dw @ np.abs(v)) / z
         # sum_j w_j |v_jd - o_d| / z <= sum_j w_j |v_jd| / z + |o_d|
         spread = (w @ np.abs(v)) / z + np.abs(oo)
         t_s = (np.exp(E) - 1.0) * np.exp(E) * spread

@@ -71,15 +71,18 @@ def _run_fp8(s, q, k, v, M, lay, hm, lse=True):
     ops8 = svg.svg_quantize_fp8(q.to(DEV), k.to(DEV), v.to(DEV), s, head_layout=layd)
     o8, l8 = svg.svg_block_sparse_attn_fp8(ops8, s, 1.0 / np.sqrt(s.D), enc, head_mask=hmd, head_layout=layd,
                                            lse=lse)
+    # without the LSE (at D = 64 the denominator is then the matrix core's
+    # sum of the E4M3 weights)
+    o8n, _ = svg.svg_block_sparse_attn_fp8(ops8, s, 1.0 / np.sqrt(s.D), enc, head_mask=hmd, head_layout=layd)
     # the bf16 path on the same inputs, for the reported distance
     kp, vt = svg.svg_prepare_kv(k.to(DEV), v.to(DEV), s, head_layout=layd)
     o16, _, _ = svg.svg_block_sparse_attn(q.to(DEV), k.to(DEV), None, s, 1.0 / np.sqrt(s.D), enc,
                                           head_mask=hmd, head_layout=layd, kp=kp, vt=vt)
     torch.cuda.synchronize()
-    return o8.cpu(), None if l8 is None else l8.cpu(), o16.cpu()
+    return o8.cpu(), None if l8 is None else l8.cpu(), o16.cpu(), o8n.cpu()
 
 
-def _check_head(s, q, k, v, M, lay, o8, l8, o16, b, h, qblocks=None, what=""):
+def _check_head(s, q, k, v, M, lay, o8, l8, o16, b, h, qblocks=None, what="", o8n=None):
     F, Hs, Ws = s.F, s.Hs, s.Ws
     bh = b * s.H + h
     scale = 1.0 / np.sqrt(s.D)
@@ -105,6 +108,17 @@ def _check_head(s, q, k, v, M, lay, o8, l8, o16, b, h, qblocks=None, what=""):
     assert worst <= 1.0, f"{what} head {bh}: error reaches {worst:.3f} of the bound"
     assert le <= 1.0, f"{what} head {bh}: lse error reaches {le:.3f} of the bound"
     assert np.array_equal(np.isneginf(g_lse[rows]), np.isneginf(ref_lse[rows]))
+    if o8n is not None:
+        got_n = to_np(o8n[b, h])
+        if s.D == 128:     # the same kernel with or without the LSE
+            assert np.array_equal(got_n, to_np(o8[b, h])), f"{what} head {bh}: output depends on the LSE request"
+        else:
+            bnd_n, _ = fp8_bound(deq[0], deq[1], deq[2], M, 128, scale, list(qbs), self_norm=True)
+            if lay[bh]:
+                got_n = got_n[np.argsort(p)]
+            worst_n = float(np.max(np.abs(got_n[rows] - ref[rows]) / bnd_n[rows]))
+            print(f"[fp8] {what} head {bh}: no-LSE call (E4M3-weight denominator) worst error / bound {worst_n:.3f}")
+            assert worst_n <= 1.0, f"{what} head {bh} (no LSE): error reaches {worst_n:.3f} of the bound"
 
 
 @pytest.mark.parametrize("D", [128, 64])
@@ -122,10 +136,10 @@ def test_fp8_attention_within_derived_bound(D):
     M[2, 5] = 1
     lay = np.array([0, 1, 1, 0, 1, 0], np.int32)
     hm = np.arange(B * H, dtype=np.int32)
-    o8, l8, o16 = _run_fp8(s, q, k, v, M, lay, hm)
+    o8, l8, o16, o8n = _run_fp8(s, q, k, v, M, lay, hm)
     for b in range(B):
         for h in range(H):
-            _check_head(s, q, k, v, M[b * H + h], lay, o8, l8, o16, b, h, what=f"D{D}")
+            _check_head(s, q, k, v, M[b * H + h], lay, o8, l8, o16, b, h, what=f"D{D}", o8n=o8n)
 
 
 def test_fp8_generator_heads_wan_shape_sampled():
@@ -138,7 +152,23 @@ def test_fp8_generator_heads_wan_shape_sampled():
     s = svg.Shape(w.B, w.H, w.N, w.D, w.F, w.Hs, w.Ws, w.block)
     cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
     lay = cls.astype(np.int32)
-    o8, l8, o16 = _run_fp8(s, q, k, v, cand, lay, lay.copy())
+    o8, l8, o16, o8n = _run_fp8(s, q, k, v, cand, lay, lay.copy())
     for h in range(w.H):
         qbs = sample_qblocks(w.n_blocks, seed=300 + h)
-        _check_head(s, q, k, v, cand[lay[h]], lay, o8, l8, o16, 0, h, qblocks=qbs, what="wan")
+        _check_head(s, q, k, v, cand[lay[h]], lay, o8, l8, o16, 0, h, qblocks=qbs, what="wan", o8n=o8n)
+
+
+def test_fp8_generator_heads_cogvideox_shape_sampled():
+    """Spatial and temporal heads of the synthetic generator at the CogVideoX
+    shape (D = 64, 4 heads) through the FP8 path with their online masks, with
+    and without the LSE; 32 query blocks per head against the bounds."""
+    banner("fp8 cogvideox heads")
+    w = S.get_workload("cogvideox", H=4, n_spatial=2)
+    q, k, v, cls = S.gen_qkv(w, dtype="bf16")
+    s = svg.Shape(w.B, w.H, w.N, w.D, w.F, w.Hs, w.Ws, w.block)
+    cand = O.online_candidate_masks(w.F, w.Hs, w.Ws, w.N, w.block, w.band_w)
+    lay = cls.astype(np.int32)
+    o8, l8, o16, o8n = _run_fp8(s, q, k, v, cand, lay, lay.copy())
+    for h in range(w.H):
+        qbs = sample_qblocks(w.n_blocks, seed=310 + h)
+        _check_head(s, q, k, v, cand[lay[h]], lay, o8, l8, o16, 0, h, qblocks=qbs, what="cogvideox", o8n=o8n)
