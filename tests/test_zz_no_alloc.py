@@ -3,7 +3,7 @@ work plan in the library's fixed device array) against svg_block_sparse_attn
 with a workspace, called through the C ABI.  Two calls in a row on the same
 GPU, the second with a smaller input (the array still holds the first call's
 plan, which the second must rewrite): outputs and log-sum-exp equal bit for
-bit.  The caller passes every output, nothing is allocated by the call."""
+bit, with and without the LSE.  The caller passes every output, nothing is allocated by the call."""
 import numpy as np
 import pytest
 import torch
@@ -45,6 +45,15 @@ def test_noalloc_equals_workspace_call_twice():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref), f"case {seed}: o differs"
         assert torch.equal(lse, l_ref), f"case {seed}: lse differs"
+        # without the LSE (the D = 64 case then sums its denominator on the
+        # matrix core): the same kernels behind both entry points
+        o2_ref, _, _ = svg.svg_block_sparse_attn(q, k, None, s, 0.1, enc, head_mask=hm, head_layout=lay,
+                                                 kp=kp, vt=vt)
+        o2 = torch.empty_like(q)
+        svg.svg_block_sparse_attn_noalloc(q, k, None, s, 0.1, enc, head_mask=hm, head_layout=lay, kp=kp,
+                                          out=o2, vt=vt)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o2_ref), f"case {seed}: o without the LSE differs"
 
 
 def test_noalloc_64_token_blocks():
