@@ -240,7 +240,9 @@ svg_status svg_prepare_kv(const void* k, const void* v, void* kp, void* vt, svg_
  * with it), with 64-token blocks it walks the skip list.  A query block whose mask row is empty gets o = 0
  * and lse = -inf.  bf16 inputs, fp32 accumulation and softmax, bf16 output
  * (P rounded to bf16 for the PV product; the softmax denominator sums the
- * fp32 weights).  The result does not depend on whether vt is given. */
+ * fp32 weights, except for 128-token blocks at D = 64 with lse == NULL,
+ * where it is the matrix core's fp32 sum of the bf16-rounded weights the PV
+ * product used).  The result does not depend on whether vt is given. */
 svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const void* vt, void* o,
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,
@@ -284,7 +286,9 @@ svg_status svg_quantize_fp8(const void* q, const void* k, const void* v, uint8_t
 /* Block-sparse attention with both products on FP8 (E4M3) operands
  * (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation): S = scale * d_q * d_k *
  * (q8 . k8), the online softmax in fp32, P rounded to E4M3 for the PV
- * product, O = d_v * sum(P v8) / sum(P) with the denominator in fp32, output
+ * product, O = d_v * sum(P v8) / sum(P) with the denominator summed from the
+ * fp32 weights (from the E4M3 weights on the matrix core at D = 64 when
+ * lse == NULL), output
  * bf16 [B,H,N,D] frame-major for every head (layout-1 heads read their Q rows
  * and write their O rows through the permutation).  q8, k8, vt8, scales as
  * svg_quantize_fp8 writes them for the same head_layout; masks, head_mask,
