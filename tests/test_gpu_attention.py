@@ -11,7 +11,7 @@ import torch
 import block_sparse_attention_svg_amd as svg
 import oracle as O
 import synth as S
-from parity_utils import banner, assert_attn_close, to_np, LSE_ABS, sample_qblocks
+from parity_utils import banner, assert_attn_close, to_np, LSE_ABS, sample_qblocks, fp8_bound
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -212,7 +212,9 @@ def test_softmax_reference_moves(order):
     """Scores that rise by ~36 (log2 units) per key block move the running
     max at every block (O and the denominator rescaled each time); falling
     scores never move it (later weights underflow towards 0); one far larger
-    block moves it once.  All rows, O and LSE, against the oracle."""
+    block moves it once.  All rows, O and LSE, against the oracle; the call
+    without LSE (denominator on the matrix core) and the FP8 variant with and
+    without LSE as well, FP8 against its derived bounds."""
     banner("attn reference", order)
     N, D, nB = 1000, 64, 8                                  # ragged last block
     rng = np.random.default_rng(17)
@@ -237,6 +239,26 @@ def test_softmax_reference_moves(order):
     assert np.all(np.isfinite(to_np(o[0, 0])))
     assert_attn_close(to_np(o[0, 0]), ref, f"reference {order}")
     assert np.max(np.abs(lse[0, 0].cpu().numpy() - ref_lse)) < LSE_ABS * max(1.0, float(np.max(np.abs(ref_lse))) / 64)
+    # without the LSE: the denominator summed on the matrix core, rescaled
+    # with O at every move of the running max
+    o2, _, _ = svg.svg_block_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), s, scale, enc, head_mask=hm)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(to_np(o2[0, 0])))
+    assert_attn_close(to_np(o2[0, 0]), ref, f"reference {order} (no LSE)")
+    # FP8, with and without the LSE, against the bounds derived from E4M3
+    ops8 = svg.svg_quantize_fp8(q.to(DEV), k.to(DEV), v.to(DEV), s)
+    o8, l8 = svg.svg_block_sparse_attn_fp8(ops8, s, scale, enc, head_mask=hm, lse=True)
+    o8n, _ = svg.svg_block_sparse_attn_fp8(ops8, s, scale, enc, head_mask=hm)
+    torch.cuda.synchronize()
+    deq = [O.quantize_head(x[0, 0].float().numpy())[3] for x in (q, k, v)]
+    ref8, ref8_lse = O.block_masked_attention(deq[0], deq[1], deq[2], masks[0], 128, scale)
+    for got, self_norm, what in ((o8, False, "fp8"), (o8n, True, "fp8 no LSE")):
+        bnd, e_lse = fp8_bound(deq[0], deq[1], deq[2], masks[0], 128, scale, list(range(nB)), self_norm=self_norm)
+        g = to_np(got[0, 0])
+        assert np.all(np.isfinite(g)), what
+        worst = float(np.max(np.abs(g - ref8) / bnd))
+        assert worst <= 1.0, f"reference {order} ({what}): error reaches {worst:.3f} of the bound"
+    assert np.all(np.abs(l8[0, 0].cpu().numpy() - ref8_lse) <= e_lse), f"reference {order}: fp8 lse"
 
 
 def test_fused_layout_equals_permuted_twins():
