@@ -512,23 +512,26 @@ __device__ __forceinline__ void mfma_pv8(const char* vb_lds, int v_lane, const i
                                          f32x16* oacc, const i32x8& sel, f32x4& lacc) {
   using C = Cfg2<D, true>;
   constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
-  i32x8 cur[C::DT], nxt[C::DT];
+  // Operand i = (group i / DT, row tile i % DT) in a ring of three: operand
+  // i + 2 is read while product i computes (24 registers instead of the 64
+  // that a whole group's operands in flight take at D = 128).
+  constexpr int NOP = C::PG * C::DT;
+  auto op_at = [&](int i) {
+    return lds_32bytes(vb_lds + v_lane + C::tile_off(i % C::DT, DT_OFF) + (i / C::DT) * 64);
+  };
+  i32x8 ring[3];
+  ring[0] = op_at(0);
+  if constexpr (NOP > 1) ring[1] = op_at(1);
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) cur[dt] = lds_32bytes(vb_lds + v_lane + C::tile_off(dt, DT_OFF));
-#pragma unroll
-  for (int g = 0; g < C::PG; ++g) {
-    if (g + 1 < C::PG) {
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-        nxt[dt] = lds_32bytes(vb_lds + v_lane + C::tile_off(dt, DT_OFF) + (g + 1) * 64);
+  for (int i = 0; i < NOP; ++i) {
+    if (i + 2 < NOP) ring[(i + 2) % 3] = op_at(i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const int g = i / C::DT, dt = i % C::DT;
+    oacc[dt] = mfma_f8(ring[i % 3], pb[g], oacc[dt]);
+    if constexpr (MS) {
+      if (dt == C::DT - 1) lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[g], lacc, 0, 0, 0, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = mfma_f8(cur[dt], pb[g], oacc[dt]);
-    if constexpr (MS) lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[g], lacc, 0, 0, 0, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) cur[dt] = nxt[dt];
   }
 }
 
@@ -1469,18 +1472,15 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.head_mask, a.head_layout, a.n_masks,
                      a.n_kb, a.BH, pairs, a.BH * per_xcd, a.plan);
   const dim3 grid(persistent_grid(int64_t(a.BH) * pairs));
-  // D = 64 is bound by the softmax's VALU work: its denominator moves to the
-  // matrix core unless the LSE is asked for (bf16 and FP8).  At D = 128 the
-  // kernels are at the register limit (the FP8 one then spills in its loop,
-  // 18 % slower at Wan) and the bf16 one is held by the board's power limit
-  // (no gain): fp32 adds.
-  if constexpr (F8 && D == 64) {
+  // The softmax's VALU work bounds the FP8 kernels and the bf16 one at
+  // D = 64: their denominators move to the matrix core unless the LSE is
+  // asked for.  The bf16 kernel at D = 128 is held by the board's power limit
+  // instead (no gain measured): fp32 adds.
+  if constexpr (F8) {
     if (a.lse == nullptr)
       hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
     else
       hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
-  } else if constexpr (F8) {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
   } else if constexpr (D == 64) {
     if (a.lse == nullptr)
       hipLaunchKernelGGL((attn_fwd_b128_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);

@@ -287,8 +287,8 @@ svg_status svg_quantize_fp8(const void* q, const void* k, const void* v, uint8_t
  * (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation): S = scale * d_q * d_k *
  * (q8 . k8), the online softmax in fp32, P rounded to E4M3 for the PV
  * product, O = d_v * sum(P v8) / sum(P) with the denominator summed from the
- * fp32 weights (from the E4M3 weights on the matrix core at D = 64 when
- * lse == NULL), output
+ * fp32 weights (from the E4M3 weights on the matrix core when lse == NULL),
+ * output
  * bf16 [B,H,N,D] frame-major for every head (layout-1 heads read their Q rows
  * and write their O rows through the permutation).  q8, k8, vt8, scales as
  * svg_quantize_fp8 writes them for the same head_layout; masks, head_mask,

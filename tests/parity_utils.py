@@ -82,7 +82,7 @@ def fp8_bound(qd, kd, vd, M, B, scale, qblocks, self_norm=False):
     the oracle's attention on the dequantized q, k, v in the mask's layout.
 
     self_norm: the output's denominator is the matrix core's sum of the E4M3
-    weights themselves (the D = 64 call without LSE) instead of the fp32
+    weights themselves (the call without LSE) instead of the fp32
     weights: o' = sum q_j v_j / sum q_j with q_j = w_j + d_j, so
     o' - o_w = sum d_j (v_j - o_w) / sum q_j, at most
     (sum |d_j| |v_j| + |o_w| sum |d_j|) / (z - sum |d_j|) (every |d_j| <= w_j
