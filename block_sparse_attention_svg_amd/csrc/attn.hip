@@ -360,8 +360,39 @@ __device__ __forceinline__ void seq_build(SeqLds& L, const uint32_t* __restrict_
   seq_scan(L, seq_words(bm0, two, W, w), W, w);
 }
 
+// S^T = K Q^T as mfma_qk, the K operands through a ring of three at D = 128
+// (operand i = (contraction step i / KT, key tile i % KT); i + 2 read while
+// product i computes).
+template <int D>
+__device__ __forceinline__ void mfma_qk_r(const char* kb_lds, int k_lane, const bf16x8* qreg,
+                                          f32x16* sacc) {
+  using C = Cfg2<D>;
+  if constexpr (D != 128) {
+    mfma_qk<D>(kb_lds, k_lane, qreg, sacc);
+  } else {
+    constexpr int NOP = C::DK * C::KT;
+    auto op_at = [&](int i) {
+      return *reinterpret_cast<const uint4*>(kb_lds + k_lane + C::tile_off_k(i % C::KT, 256) + (i / C::KT) * 32);
+    };
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) sacc[kt] = f32x16{};
+    uint4 ring[3];
+    ring[0] = op_at(0);
+    ring[1] = op_at(1);
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      if (i + 2 < NOP) ring[(i + 2) % 3] = op_at(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kk = i / C::KT, kt = i % C::KT;
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ring[i % 3]), qreg[kk], sacc[kt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // O^T (D x 32 queries) += V^T P^T, the V^T operands of key step s+1 in flight
-// while step s computes.  With MS (matrix-core sum) every step also adds its
+// while step s computes (at D = 128 a ring of three operands instead, which
+// frees 20 registers there).  With MS (matrix-core sum) every step also adds its
 // 16 keys' weights into the denominator on the matrix core: one
 // v_mfma_f32_16x16x32_bf16 with the weights as the B operand and the 0/1
 // selector `sel` as A (lane l: rows 4i of A take the contraction groups
@@ -373,6 +404,29 @@ __device__ __forceinline__ void mfma_pv(const char* vb_lds, int v_lane, const bf
                                         f32x16* oacc, const bf16x8& sel, f32x4& lacc) {
   using C = Cfg2<D>;
   constexpr int DT_OFF = 32 / C::VNI * C::VW;   // V^T rows +32
+  if constexpr (D == 128) {
+    // operand i = (key step i / DT, row tile i % DT) in a ring of three:
+    // operand i + 2 is read while product i computes
+    constexpr int NOP = C::PS * C::DT;
+    auto op_at = [&](int i) {
+      return *reinterpret_cast<const uint4*>(vb_lds + v_lane + (i % C::DT) * DT_OFF + (i / C::DT) * 32);
+    };
+    uint4 ring[3];
+    ring[0] = op_at(0);
+    ring[1] = op_at(1);
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      if (i + 2 < NOP) ring[(i + 2) % 3] = op_at(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int s = i / C::DT, dt = i % C::DT;
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ring[i % 3]), pb[s], oacc[dt], 0, 0, 0);
+      if constexpr (MS) {
+        if (dt == C::DT - 1) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[s], lacc, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
   uint4 cur[C::DT], nxt[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
@@ -746,7 +800,7 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
     // ---- phase 1 --------------------------------------------------------------
     if (grp == 0) {
       if (have_prev && mine_prev) mfma_pv<D, MS>(v_prev, v_lane, pb, oacc, sel, lacc);
-      if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
+      if (have_cur && mine_cur) mfma_qk_r<D>(k_cur, k_lane, qreg, sacc);
     } else {
       if (have_prev && mine_prev)
         softmax_block<D, MS>(sacc, pb, oacc, m_run, l_part, lacc, kb_prev * C::BLK, N, h, c2);
@@ -768,7 +822,7 @@ __device__ __forceinline__ void attn_pair(const AttnArgs& a, int bh, int pair, i
         softmax_block<D, MS>(sacc, pb, oacc, m_run, l_part, lacc, kb_cur * C::BLK, N, h, c2);
     } else {
       if (have_prev && mine_prev) mfma_pv<D, MS>(v_prev, v_lane, pb, oacc, sel, lacc);
-      if (have_cur && mine_cur) mfma_qk<D>(k_cur, k_lane, qreg, sacc);
+      if (have_cur && mine_cur) mfma_qk_r<D>(k_cur, k_lane, qreg, sacc);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
@@ -1472,22 +1526,20 @@ void launch_b128(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(order_kernel, dim3(8), dim3(256), 0, st, a.head_mask, a.head_layout, a.n_masks,
                      a.n_kb, a.BH, pairs, a.BH * per_xcd, a.plan);
   const dim3 grid(persistent_grid(int64_t(a.BH) * pairs));
-  // The softmax's VALU work bounds the FP8 kernels and the bf16 one at
-  // D = 64: their denominators move to the matrix core unless the LSE is
-  // asked for.  The bf16 kernel at D = 128 is held by the board's power limit
-  // instead (no gain measured): fp32 adds.
+  // The denominators move to the matrix core unless the LSE is asked for:
+  // the softmax's VALU work bounds the FP8 kernels and the bf16 one at
+  // D = 64; the bf16 one at D = 128, held by the board's power limit, gains
+  // less (0.6 %).
   if constexpr (F8) {
     if (a.lse == nullptr)
       hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
     else
       hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
-  } else if constexpr (D == 64) {
+  } else {
     if (a.lse == nullptr)
       hipLaunchKernelGGL((attn_fwd_b128_kernel<D, true>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
     else
       hipLaunchKernelGGL((attn_fwd_b128_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
-  } else {
-    hipLaunchKernelGGL((attn_fwd_b128_kernel<D, false>), grid, dim3(512), 0, st, a, a.BH * per_xcd);
   }
 }
 

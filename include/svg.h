@@ -240,9 +240,9 @@ svg_status svg_prepare_kv(const void* k, const void* v, void* kp, void* vt, svg_
  * with it), with 64-token blocks it walks the skip list.  A query block whose mask row is empty gets o = 0
  * and lse = -inf.  bf16 inputs, fp32 accumulation and softmax, bf16 output
  * (P rounded to bf16 for the PV product; the softmax denominator sums the
- * fp32 weights, except for 128-token blocks at D = 64 with lse == NULL,
- * where it is the matrix core's fp32 sum of the bf16-rounded weights the PV
- * product used).  The result does not depend on whether vt is given. */
+ * fp32 weights, except for 128-token blocks with lse == NULL, where it is
+ * the matrix core's fp32 sum of the bf16-rounded weights the PV product
+ * used).  The result does not depend on whether vt is given. */
 svg_status svg_block_sparse_attn(const void* q, const void* k, const void* v, const void* vt, void* o,
                                  const void* qp, const void* kp, const void* vp, void* op,
                                  svg_shape s, float scale, const svg_mask* masks,

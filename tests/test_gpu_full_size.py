@@ -40,8 +40,8 @@ def _online(name, workload_inputs):
         o, lse = layer(q.to(DEV), k.to(DEV), v.to(DEV), idx, lse=True)
         torch.cuda.synchronize()
         choice = layer.choice.cpu().numpy()
-        # the bench's call: no LSE (at D = 64 the denominator is then summed
-        # on the matrix core from the bf16 weights)
+        # the bench's call: no LSE (the denominator is then summed on the
+        # matrix core from the bf16 weights)
         o2, _ = layer(q.to(DEV), k.to(DEV), v.to(DEV), idx)
         torch.cuda.synchronize()
         assert np.array_equal(layer.choice.cpu().numpy(), choice)
@@ -84,12 +84,9 @@ def test_online_layer_every_head(name, part, n_parts, workload_inputs):
         g_lse = r["lse"][0, h].numpy()
         g_lse = g_lse[p] if lay == 1 else g_lse          # stored in the attended layout
         le = float(np.max(np.abs(g_lse[rows] - ref_lse[rows])))
-        # without the LSE: the same kernel at D = 128 (bit-equal output), the
-        # matrix-core denominator at D = 64
+        # without the LSE: the denominator summed on the matrix core
         got2 = to_np(r["o_nolse"][0, h])[rows]
         mx2, rl2 = attn_errors(got2, ref[rows])
-        if w.D == 128:
-            assert np.array_equal(got2, got), f"{name} head {h}: output depends on the LSE request"
         print(f"[parity] {name} head {h} ({'TS'[lay]}) {len(qbs)} blocks {int(rows.sum())} rows: "
               f"max-abs {mx:.3e} rel-L2 {rl:.3e} lse {le:.3e}; no-LSE call max-abs {mx2:.3e} rel-L2 {rl2:.3e}")
         worst = [max(worst[0], mx, mx2), max(worst[1], rl, rl2), max(worst[2], le)]

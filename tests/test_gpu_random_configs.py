@@ -64,8 +64,8 @@ def test_random_config_matches_oracle(seed):
         kp, vt = svg.svg_prepare_kv(kd, vd, s, head_layout=layd)
         o, _, lse = svg.svg_block_sparse_attn(qd, kd, None, s, scale, enc, head_mask=hm, head_layout=layd,
                                               kp=kp, vt=vt, lse=True)
-        # without the LSE (at D = 64 the denominator is then summed on the
-        # matrix core from the bf16 weights)
+        # without the LSE (the denominator is then summed on the matrix core
+        # from the bf16 weights)
         o2, _, _ = svg.svg_block_sparse_attn(qd, kd, None, s, scale, enc, head_mask=hm, head_layout=layd,
                                              kp=kp, vt=vt)
         outs = [o, o2]
@@ -88,8 +88,6 @@ def test_random_config_matches_oracle(seed):
             if s.block == 128:
                 got2 = to_np(outs[1][b, h])
                 assert_attn_close(got2, ref, f"seed {seed} head {bh} (no LSE)")
-                if s.D == 128:
-                    assert np.array_equal(got2, got), f"seed {seed} head {bh}: output depends on the LSE request"
             g = lse[b, h].cpu().numpy()
             fin = np.isfinite(ref_lse)
             assert np.array_equal(np.isneginf(g), ~fin), f"seed {seed} head {bh}: empty rows"

@@ -45,8 +45,8 @@ def test_noalloc_equals_workspace_call_twice():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref), f"case {seed}: o differs"
         assert torch.equal(lse, l_ref), f"case {seed}: lse differs"
-        # without the LSE (the D = 64 case then sums its denominator on the
-        # matrix core): the same kernels behind both entry points
+        # without the LSE (the denominator is then summed on the matrix
+        # core): the same kernels behind both entry points
         o2_ref, _, _ = svg.svg_block_sparse_attn(q, k, None, s, 0.1, enc, head_mask=hm, head_layout=lay,
                                                  kp=kp, vt=vt)
         o2 = torch.empty_like(q)
