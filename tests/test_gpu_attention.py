@@ -79,15 +79,17 @@ def test_ragged_partial_blocks_and_empty_rows():
     masks[:, :, 2] = 1
     masks[1, 1] = 0                     # empty row
     o, _, lse = _run_heads(w, q, k, v, masks, [0, 0, 0], block=128, lse=True)
+    o2, _, _ = _run_heads(w, q, k, v, masks, [0, 0, 0], block=128)     # denominator on the matrix core
     for h in range(3):
         ref, ref_lse = O.block_masked_attention(q[0, h].float().numpy(), k[0, h].float().numpy(),
                                                 v[0, h].float().numpy(), masks[h], 128, w.scale)
         assert_attn_close(to_np(o[0, h]), ref, f"ragged head {h}")
+        assert_attn_close(to_np(o2[0, h]), ref, f"ragged head {h} (no LSE)")
         g = lse[0, h].cpu().numpy()
         fin = np.isfinite(ref_lse)
         assert np.array_equal(np.isneginf(g), ~fin)
         assert np.max(np.abs(g[fin] - ref_lse[fin])) < LSE_ABS
-    assert torch.all(o[0, 1, 128:256] == 0)
+    assert torch.all(o[0, 1, 128:256] == 0) and torch.all(o2[0, 1, 128:256] == 0)
 
 
 @pytest.mark.parametrize("D,block", [(64, 64), (128, 64), (64, 128)])
@@ -195,6 +197,7 @@ def test_long_rows_cross_block_list_windows():
     hm = torch.arange(2, dtype=torch.int32, device=DEV)
     o, _, lse = svg.svg_block_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), s, w.scale, enc,
                                           head_mask=hm, lse=True)
+    o2, _, _ = svg.svg_block_sparse_attn(q.to(DEV), k.to(DEV), v.to(DEV), s, w.scale, enc, head_mask=hm)
     torch.cuda.synchronize()
     qbs = [0, 10, 11, 20, 21, 1024, nB - 2, nB - 1]
     for h in range(2):
@@ -203,6 +206,7 @@ def test_long_rows_cross_block_list_windows():
                                                 qblocks=qbs)
         rows = ~np.isnan(ref[:, 0])
         assert_attn_close(to_np(o[0, h])[rows], ref[rows], f"long rows head {h}")
+        assert_attn_close(to_np(o2[0, h])[rows], ref[rows], f"long rows head {h} (no LSE)")
         g = lse[0, h].cpu().numpy()[rows]
         assert np.max(np.abs(g - ref_lse[rows])) < LSE_ABS
 
