@@ -1097,15 +1097,13 @@ __device__ __forceinline__ void attn_pair_f8(const AttnArgs& a, int bh, int pair
     // The groups share no data within an iteration (each holds its own S, P
     // and O; the copies of this iteration refill buffers last read in the
     // previous one).  With FP8 products the matrix-core phase is short, and
-    // at D = 128 a group that started its softmax early would run it beside
-    // the other group's (both then slower on the shared VALU): the groups
-    // meet between the phases there (1.5 % faster at Wan and Hunyuan, 1.6 %
-    // slower at D = 64).
+    // a group that started its softmax early would run it beside the other
+    // group's (both then slower on the shared VALU): the groups meet between
+    // the phases (1.4-2.2 % faster at Wan, 3 % at CogVideoX with the
+    // denominator on the matrix core).
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (D == 128) {
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     // ---- phase 2 --------------------------------------------------------------
     if (grp == 0) {
       // K of block j+1 into the K buffer freed by block j-1, V^T of block j
